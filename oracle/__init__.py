@@ -1,0 +1,115 @@
+"""Float64 CPU oracle for decode-time gated delta-rule recurrences.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+package.  It shares no code with the GPU library, and the GPU library never
+falls back to it.
+
+* :func:`run` -- the plain step-by-step recurrence in float64 (C, OpenMP over
+  independent states; ``recurrence.c``).  It follows the operator list of the
+  DeltaLog page (Technical Summary, Kernel Implementation) with the update
+  formulas written out in ``recurrence.c``.
+* :mod:`oracle.exact` -- exact rational (``fractions.Fraction``) models used
+  to pin the float64 oracle and the deferred base + log algebra.
+
+Parity status: every function here is pinned by the CPU tests
+(``tests/test_oracle_pins.py``): brute-force product expansion, the
+delta-rule write invariant, the identity case, closed forms and the exact
+equality of eager and deferred schedules.  The pages print no worked numeric
+example, so no stored value comes from them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH, build_oracle, needs_build
+
+GDN, KDA, RWKV6 = 0, 1, 2
+
+_libs: dict = {}
+
+
+def _load(path: str | None = None):
+    """Load the oracle library (``path`` overrides it, e.g. for mutation tests)."""
+    key = path or LIB_PATH
+    if key not in _libs:
+        if path is None and needs_build():
+            build_oracle()
+        lib = ctypes.CDLL(key)
+        lib.oracle_run.restype = ctypes.c_int
+        lib.oracle_run.argtypes = [
+            ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int,
+        ]
+        lib.oracle_max_threads.restype = ctypes.c_int
+        _libs[key] = lib
+    return _libs[key]
+
+
+def default_threads() -> int:
+    """Every core in this process's affinity mask."""
+    return len(os.sched_getaffinity(0))
+
+
+def _f32(a):
+    return None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def run(variant: int, q, k, v, g, beta=None, S0=None, t_start=None, threads: int | None = None,
+        lib_path: str | None = None):
+    """Run the recurrence for ``P`` independent states over ``T`` steps.
+
+    Shapes: ``q, k`` ``[T, P, d_k]``; ``v`` ``[T, P, d_v]``; ``g`` ``[T, P]``
+    (head-wise decay) or ``[T, P, d_k]`` (channel-wise); ``beta`` ``[T, P]``
+    (not used by the additive variant); ``S0`` ``[P, d_v, d_k]`` or None for
+    zeros; ``t_start`` ``[P]`` first step each state takes (outputs before it
+    are zero).  All float inputs are the exact values the kernels consume.
+
+    Returns ``(o, S)``: float64 ``[T, P, d_v]`` and ``[P, d_v, d_k]``.
+    """
+    q, k, v, g, beta, S0 = (_f32(x) for x in (q, k, v, g, beta, S0))
+    T, P, dk = q.shape
+    dv = v.shape[2]
+    assert k.shape == (T, P, dk) and v.shape == (T, P, dv)
+    if variant == GDN:
+        assert g.shape == (T, P)
+    else:
+        assert g.shape == (T, P, dk)
+    if variant != RWKV6:
+        assert beta is not None and beta.shape == (T, P)
+    else:
+        beta = None
+    if S0 is not None:
+        assert S0.shape == (P, dv, dk)
+    ts = None
+    if t_start is not None:
+        ts = np.ascontiguousarray(t_start, dtype=np.int32)
+        assert ts.shape == (P,)
+    o = np.zeros((T, P, dv), dtype=np.float64)
+    S = np.zeros((P, dv, dk), dtype=np.float64)
+    rc = _load(lib_path).oracle_run(variant, P, dk, dv, T, _ptr(S0), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(g), _ptr(beta), _ptr(ts), _ptr(o), _ptr(S),
+                            int(threads or default_threads()))
+    if rc != 0:
+        raise RuntimeError(f"oracle_run failed with code {rc}")
+    return o, S
+
+
+def readout(S, q):
+    """``o = S q`` for states ``[P, d_v, d_k]`` and queries ``[P, d_k]`` (float64)."""
+    S = np.asarray(S, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    return np.einsum("pij,pj->pi", S, q)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())

@@ -1,0 +1,291 @@
+"""Exact rational models of the recurrences and of the deferred schedule.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Everything here works
+on ``fractions.Fraction`` values in plain Python lists, for tiny sizes only
+(``d <= 8``, ``T <= 16``).  Decays enter as ``alpha`` itself (a positive
+rational), so every result is exact.
+
+Notation: a state ``S`` is a ``d_v x d_k`` list of rows; vectors are lists.
+Variants: 0 = Gated DeltaNet (scalar ``alpha``), 1 = KDA (per-key-channel
+``alpha``), 2 = RWKV6-style additive (per-channel ``w``, no ``beta``).
+
+Sources:
+
+* the step formulas are the ones written in ``recurrence.c``; the
+  DeltaLog page ("DeltaLog: Deferred Materialization of Recurrent States for
+  Linear Attention Decoding", Technical Summary, Kernel Implementation)
+  names the three operators and their decay granularity;
+* the deferred schedule -- a read-only dense base, a bounded log of compact
+  per-token updates appended every step, a periodic merge that materialises
+  base plus log and resets the log -- is the DeltaLog page's Core Mechanism;
+  its claim that this only changes the physical schedule, not the
+  recurrence (Methodology), is what :func:`deferred_run` is tested against;
+* the merge is written in WY/UT form: a product of rank-one delta-rule
+  transforms folded into one triangular solve, the block form the CARVE page
+  (abstract) and its Gated DeltaNet-2 neighbour (chunkwise WY algorithm)
+  refer to.
+"""
+from __future__ import annotations
+
+from fractions import Fraction as Fr
+
+GDN, KDA, RWKV6 = 0, 1, 2
+
+
+# ----------------------------------------------------------------------------
+# small exact linear algebra
+# ----------------------------------------------------------------------------
+def zeros(r, c):
+    return [[Fr(0)] * c for _ in range(r)]
+
+
+def eye(n):
+    return [[Fr(int(i == j)) for j in range(n)] for i in range(n)]
+
+
+def matmul(A, B):
+    n, m, p = len(A), len(B), len(B[0])
+    assert all(len(row) == m for row in A)
+    return [[sum((A[i][t] * B[t][j] for t in range(m)), Fr(0)) for j in range(p)]
+            for i in range(n)]
+
+
+def matvec(A, x):
+    return [sum((a * b for a, b in zip(row, x)), Fr(0)) for row in A]
+
+
+def dot(a, b):
+    return sum((x * y for x, y in zip(a, b)), Fr(0))
+
+
+def outer(a, b):
+    return [[x * y for y in b] for x in a]
+
+
+def madd(A, B, c=Fr(1)):
+    return [[x + c * y for x, y in zip(ra, rb)] for ra, rb in zip(A, B)]
+
+
+def diag(v):
+    n = len(v)
+    return [[v[i] if i == j else Fr(0) for j in range(n)] for i in range(n)]
+
+
+def _chan(variant, alpha, dk):
+    """Per-key-channel decay vector (a scalar decay is repeated)."""
+    if variant == GDN:
+        return [Fr(alpha)] * dk
+    assert len(alpha) == dk
+    return [Fr(a) for a in alpha]
+
+
+# ----------------------------------------------------------------------------
+# eager recurrence
+# ----------------------------------------------------------------------------
+def transform(variant, alpha, beta, k):
+    """The right factor ``A_t`` acting on the old state.
+
+    GDN ``alpha (I - beta k k^T)``; KDA ``diag(alpha) (I - beta k k^T)``;
+    RWKV6 ``diag(w)``.
+    """
+    dk = len(k)
+    D = diag(_chan(variant, alpha, dk))
+    if variant == RWKV6:
+        return D
+    return matmul(D, madd(eye(dk), outer(k, k), -Fr(beta)))
+
+
+def write_term(variant, beta, k, v):
+    """The additive term: ``beta v k^T`` (RWKV6: ``v k^T``)."""
+    c = Fr(1) if variant == RWKV6 else Fr(beta)
+    return [[c * x for x in row] for row in outer(v, k)]
+
+
+def step(variant, S, q, k, v, alpha, beta):
+    """``S_t = S_{t-1} A_t + write``; returns ``(S_t, o_t = S_t q_t)``."""
+    S1 = madd(matmul(S, transform(variant, alpha, beta, k)), write_term(variant, beta, k, v))
+    return S1, matvec(S1, q)
+
+
+def run_stepwise(variant, S0, qs, ks, vs, alphas, betas):
+    """Step-by-step exact recurrence; returns ``(outputs, final state)``."""
+    S = [list(r) for r in S0]
+    outs = []
+    for t in range(len(ks)):
+        b = None if betas is None else betas[t]
+        S, o = step(variant, S, qs[t], ks[t], vs[t], alphas[t], b)
+        outs.append(o)
+    return outs, S
+
+
+def run_product_expansion(variant, S0, ks, vs, alphas, betas):
+    """Brute force: ``S_T = S_0 A_1...A_T + sum_j write_j A_{j+1}...A_T``.
+
+    Every transform is built as an explicit matrix and multiplied out; no
+    step reuses a previous state.
+    """
+    T = len(ks)
+    dk = len(ks[0])
+    A = [transform(variant, alphas[t], None if betas is None else betas[t], ks[t])
+         for t in range(T)]
+
+    def prod(a, b):  # A_a ... A_{b-1} (0-based, identity when empty)
+        P = eye(dk)
+        for t in range(a, b):
+            P = matmul(P, A[t])
+        return P
+
+    S = matmul(S0, prod(0, T))
+    for j in range(T):
+        w = write_term(variant, None if betas is None else betas[j], ks[j], vs[j])
+        S = madd(S, matmul(w, prod(j + 1, T)))
+    return S
+
+
+# ----------------------------------------------------------------------------
+# deferred (base + log) schedule
+# ----------------------------------------------------------------------------
+def qchain_readout(variant, base, log, q):
+    """Readout of base + log without materialising the state.
+
+    Pulls ``q`` back through the logged transforms, newest first:
+    ``coef_j = beta_j k_j . q_j`` (RWKV6: ``k_j . q_j``) and
+    ``q_{j-1} = alpha_j * (q_j - coef_j k_j)`` (RWKV6: ``w_j * q_j``); then
+    ``o = base q_0 + sum_j coef_j v_j``.  ``log`` holds
+    ``(k, v, alpha, beta)`` tuples, oldest first.
+    """
+    dk = len(q)
+    qq = [Fr(x) for x in q]
+    coef = [Fr(0)] * len(log)
+    for j in range(len(log) - 1, -1, -1):
+        k, v, alpha, beta = log[j]
+        a = _chan(variant, alpha, dk)
+        if variant == RWKV6:
+            coef[j] = dot(k, qq)
+            qq = [ai * x for ai, x in zip(a, qq)]
+        else:
+            coef[j] = Fr(beta) * dot(k, qq)
+            qq = [ai * (x - coef[j] * kk) for ai, x, kk in zip(a, qq, k)]
+    o = matvec(base, qq)
+    for j, (k, v, alpha, beta) in enumerate(log):
+        o = [x + coef[j] * vv for x, vv in zip(o, v)]
+    return o
+
+
+def wy_merge(variant, base, log):
+    """Materialise ``base`` followed by the logged updates in WY/UT form.
+
+    With ``P_j`` the decay accumulated over entries ``1..j`` and
+    ``D(i, j) = P_j / P_i`` (products of the logged decays):
+
+    * ``W_j = base (k_j * P_j)``;
+    * ``M_ij = beta_j sum_c k_i[c] k_j[c] D(i, j)[c]`` for ``i < j``;
+    * ``U`` solves ``U (I + M) = (V - W) diag(beta)`` (forward substitution
+      over columns);
+    * ``S' = base diag(P_n) + sum_j U_j (k_j * D(j, n))^T``.
+
+    RWKV6 has no delta correction: ``U = V``.
+    """
+    n = len(log)
+    if n == 0:
+        return [list(r) for r in base]
+    dk = len(log[0][0])
+    decays = [_chan(variant, e[2], dk) for e in log]
+    P = []
+    acc = [Fr(1)] * dk
+    for a in decays:
+        acc = [x * y for x, y in zip(acc, a)]
+        P.append(acc)
+
+    def D(i, j):  # product of decays of entries i+1..j
+        out = [Fr(1)] * dk
+        for m in range(i + 1, j + 1):
+            out = [x * y for x, y in zip(out, decays[m])]
+        return out
+
+    ks = [[Fr(x) for x in e[0]] for e in log]
+    vs = [[Fr(x) for x in e[1]] for e in log]
+    if variant == RWKV6:
+        U = vs
+    else:
+        betas = [Fr(e[3]) for e in log]
+        W = [matvec(base, [kk * p for kk, p in zip(ks[j], P[j])]) for j in range(n)]
+        M = [[Fr(0)] * n for _ in range(n)]
+        for i in range(n):
+            for j in range(i + 1, n):
+                dij = D(i, j)
+                M[i][j] = betas[j] * sum((a * b * c for a, b, c in zip(ks[i], ks[j], dij)), Fr(0))
+        B = [[betas[j] * (vv - ww) for vv, ww in zip(vs[j], W[j])] for j in range(n)]
+        U = []
+        for j in range(n):
+            col = list(B[j])
+            for i in range(j):
+                col = [c - u * M[i][j] for c, u in zip(col, U[i])]
+            U.append(col)
+    last = n - 1
+    S = [[x * p for x, p in zip(row, P[last])] for row in base]
+    for j in range(n):
+        kd = [kk * d for kk, d in zip(ks[j], D(j, last))]
+        S = madd(S, outer(U[j], kd))
+    return S
+
+
+def deferred_run(variant, S0, qs, ks, vs, alphas, betas, L):
+    """Base + bounded log of ``L`` slots, merged when full.
+
+    Each step appends ``(k, v, alpha, beta)`` and reads out through the
+    q-chain with every logged entry (the current one included); when the log
+    holds ``L`` entries after the readout, it is merged into the base and
+    emptied.  Returns ``(outputs, materialised final state, final fill)``.
+    """
+    base = [list(r) for r in S0]
+    log = []
+    outs = []
+    for t in range(len(ks)):
+        b = None if betas is None else betas[t]
+        log.append((ks[t], vs[t], alphas[t], b))
+        outs.append(qchain_readout(variant, base, log, qs[t]))
+        if len(log) == L:
+            base = wy_merge(variant, base, log)
+            log = []
+    fill = len(log)
+    return outs, wy_merge(variant, base, log), fill
+
+
+def compact_wy_T(betas, ks):
+    """``T`` with ``prod_j (I - beta_j k_j k_j^T) = I - K T K^T`` (K = [k_1..k_n]).
+
+    Forward accumulation: ``T_jj = beta_j``,
+    ``T[:j, j] = -beta_j T[:j, :j] K[:, :j]^T k_j``.
+    """
+    n = len(ks)
+    T = [[Fr(0)] * n for _ in range(n)]
+    for j in range(n):
+        T[j][j] = Fr(betas[j])
+        z = [dot(ks[i], ks[j]) for i in range(j)]
+        for i in range(j):
+            T[i][j] = -Fr(betas[j]) * sum((T[i][m] * z[m] for m in range(j)), Fr(0))
+    return T
+
+
+# ----------------------------------------------------------------------------
+# schedule
+# ----------------------------------------------------------------------------
+def schedule(L, offset, steps):
+    """Slot written and merge decision per step for one sequence.
+
+    A sequence whose log already holds ``offset`` entries writes slot
+    ``(offset + t) mod L`` at step ``t`` and is merged after that step iff
+    ``(offset + t + 1) mod L == 0``.  Returns a list of
+    ``(slot, merge_after, fill_after_step_and_merge)``.
+    """
+    out = []
+    fill = offset
+    for t in range(steps):
+        slot = fill
+        fill += 1
+        merged = fill == L
+        if merged:
+            fill = 0
+        out.append((slot, merged, fill))
+    return out

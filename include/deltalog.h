@@ -1,0 +1,191 @@
+/*
+ * deltalog.h -- C ABI of the MI355X (gfx950) decode-time recurrent-state
+ * library for gated delta-rule linear attention.
+ *
+ * The operation (the DeltaLog page, "DeltaLog: Deferred Materialization of
+ * Recurrent States for Linear Attention Decoding", Technical Summary):
+ *
+ *   Problem:   every decode step folds one token's compact update (q, k, v,
+ *              a decay and, for delta-rule operators, a write strength beta)
+ *              into a fixed-size per-head state; eager decoding rewrites the
+ *              whole dense state to HBM each step.
+ *   Operators (Kernel Implementation): head-wise scalar decay with the
+ *              delta-rule correction (Gated DeltaNet), per-key decay with the
+ *              correction (KDA), per-key decay with raw-value updates (RWKV6).
+ *   Core Mechanism: the live state is a dense base plus a bounded log of
+ *              compact updates; appends leave the base untouched, and a
+ *              periodic merge materialises base + log into a new base.
+ *
+ * With S the d_v x d_k state of one (sequence, head) -- row i = value
+ * channel, column j = key channel -- and alpha = exp(g):
+ *
+ *   GDN    S' = alpha S (I - beta k k^T) + beta v k^T
+ *   KDA    S' = S diag(alpha) (I - beta k k^T) + beta v k^T
+ *   RWKV6  S' = S diag(w) + v k^T          (w = exp(g), per key channel)
+ *   every step reads out o = S' q.
+ *
+ * Memory.  The caller owns all device memory (e.g. torch tensors): one state
+ * block of dl_state_bytes() bytes, and every input and output.  The handle
+ * holds host metadata only; the memory must outlive it.
+ *
+ * Streams.  Every call that launches work is asynchronous on `stream` (a
+ * hipStream_t passed as void*, NULL = the null stream) and never
+ * synchronises, except dl_state_check.  Use one handle from one stream at a
+ * time.
+ *
+ * Rows.  A step call processes `rows` sequences at once.  Input row r
+ * updates state unit slot_idx[r] (a device int32 array), or unit r when
+ * slot_idx is NULL (then rows <= units).  Two rows of one call must not
+ * name the same unit (undefined result).  A slot index outside [0, units)
+ * makes that row write NaN to its outputs, leave every state untouched and
+ * raise DL_FLAG_BAD_SLOT.
+ *
+ * Errors.  Host-side validation failures return a non-zero dl_status
+ * without launching anything; dl_last_error() describes the latest one on
+ * the calling thread.  Conditions only the GPU can see set bits in a device
+ * flag word that dl_state_check() reads.  Faults in device code surface at
+ * the caller's next synchronisation.  No C++ exception crosses this ABI.
+ */
+#ifndef DELTALOG_H
+#define DELTALOG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DL_OK = 0,
+    DL_ERR_INVALID = 1,      /* null or misaligned pointer, bad count, argument wrong for the variant */
+    DL_ERR_UNSUPPORTED = 2,  /* well-formed but not built: d_k != d_v, d not in {64, 128}, L > 64 */
+    DL_ERR_SIZE = 3,         /* caller memory smaller than dl_state_bytes() */
+    DL_ERR_LAUNCH = 4,       /* the HIP runtime rejected a launch or copy */
+    DL_ERR_STATE = 5         /* dl_state_check found device flags set */
+} dl_status;
+
+typedef enum { DL_GDN = 0, DL_KDA = 1, DL_RWKV6 = 2 } dl_variant;
+typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
+
+typedef enum {
+    DL_MERGE_FULL = 0,       /* merge units whose log holds exactly L entries */
+    DL_MERGE_ALL = 1         /* merge every unit with a non-empty log (flush) */
+} dl_merge_mode;
+
+/* Device flag bits (dl_state_check). */
+#define DL_FLAG_LOG_FULL   0x1  /* dl_decode_step_log met a full log: row skipped, o = NaN */
+#define DL_FLAG_LOG_NONEMPTY 0x2 /* dl_decode_step_eager met a non-empty log: row skipped, o = NaN */
+#define DL_FLAG_BAD_SLOT   0x4  /* a slot index outside [0, units): row skipped, o = NaN */
+
+/* Shape of one state block. */
+typedef struct {
+    int32_t variant;   /* dl_variant */
+    int32_t units;     /* state slots (sequences), >= 1 */
+    int32_t heads;     /* heads per unit, >= 1 */
+    int32_t d_k;       /* key channels: 64 or 128 */
+    int32_t d_v;       /* value channels: must equal d_k */
+    int32_t log_len;   /* L, log slots per (unit, head): 0 (eager only) .. 64 */
+    int32_t in_dtype;  /* dl_dtype of q, k, v and of the logged k, v copies */
+} dl_desc;
+
+/* Device pointers into a state block (all row-major, contiguous).
+ *   base     [units, H, d_v, d_k] fp32  -- the dense state (eager) or base (DeltaLog)
+ *   log_k    [units, H, L, d_k] in_dtype -- logged keys, bit copies of the inputs
+ *   log_v    [units, H, L, d_v] in_dtype -- logged values
+ *   log_g    [units, H, L] (GDN) or [units, H, L, d_k] (KDA, RWKV6) fp32 log-decays
+ *   log_beta [units, H, L] fp32 (NULL for RWKV6)
+ *   fill     [units, H] int32 -- entries in each log; every head of a unit
+ *            advances together, one writer per counter
+ *   flags    [1] int32 -- DL_FLAG_* bits
+ * log_* are NULL when L == 0. */
+typedef struct {
+    float *base;
+    void *log_k;
+    void *log_v;
+    float *log_g;
+    float *log_beta;
+    int32_t *fill;
+    int32_t *flags;
+} dl_state_ptrs;
+
+typedef struct dl_state dl_state;   /* opaque host handle */
+
+/* Bytes of device memory a state block of this shape needs (0 if the
+ * descriptor is invalid or unsupported). */
+size_t dl_state_bytes(const dl_desc *desc);
+
+/* Bind a state block to caller memory `dev_mem` (256-byte aligned, at least
+ * dl_state_bytes(desc) bytes) and zero all of it on `stream` (base = 0,
+ * logs empty, flags clear).  Write an initial base through dl_state_view
+ * after this call (on the same stream, or after synchronising).
+ * On success *out owns a new handle; free it with dl_state_free. */
+dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void *stream,
+                         dl_state **out);
+
+/* Release the handle (not the device memory). NULL is accepted. */
+dl_status dl_state_free(dl_state *st);
+
+/* Device pointers of the block's parts. */
+dl_status dl_state_view(const dl_state *st, dl_state_ptrs *out);
+
+/* Eager step (the "eager" decoding the DeltaLog page's Problem section
+ * describes): for each row, read the dense state once, apply the operator,
+ * write the whole state back and emit o = S' q.  The unit's log must be
+ * empty (else DL_FLAG_LOG_NONEMPTY).
+ *   q, k   [rows, H, d_k] in_dtype         v [rows, H, d_v] in_dtype
+ *   g      [rows, H] (GDN) or [rows, H, d_k] (KDA, RWKV6) fp32 log-decay
+ *   beta   [rows, H] fp32 (GDN, KDA; ignored and may be NULL for RWKV6)
+ *   o      [rows, H, d_v] fp32 output (must not alias any input or the state)
+ * q, k, v, g, o must be 16-byte aligned; beta and slot_idx 4-byte aligned. */
+dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                               const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float *o, void *stream);
+
+/* DeltaLog step (the page's Append Phase): append (k, v, g, beta) to slot
+ * fill of each row's log without writing the base, then read out
+ * o = S_logical q from the read-only base plus the log, the new entry
+ * included.  When the log now holds L entries it is full: call dl_merge
+ * (DL_MERGE_FULL) before the unit's next step, or that step is skipped with
+ * DL_FLAG_LOG_FULL.  Arguments as for dl_decode_step_eager; needs L >= 1. */
+dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                             const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *o, void *stream);
+
+/* Merge (the page's Merge Phase): materialise base + log into the base and
+ * empty the log, for the selected rows' units (DL_MERGE_FULL: units whose
+ * log holds L entries; DL_MERGE_ALL: every non-empty log).  The update is
+ * applied in WY/UT form -- the logged rank-one transforms folded into one
+ * triangular solve and two dense contractions on the matrix cores -- the
+ * block form the CARVE page (abstract) and Gated DeltaNet-2 (chunkwise WY
+ * algorithm) use. */
+dl_status dl_merge(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
+                   void *stream);
+
+/* Same result as dl_merge, computed by replaying the logged steps one by
+ * one on the vector ALUs (a cross-check of the WY path; also a fallback for
+ * callers who prefer its rounding). */
+dl_status dl_merge_replay(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
+                          void *stream);
+
+/* Readout without an update: o = S_logical q for each row's unit, from the
+ * base and whatever the log holds (for an eager state, o = S q).
+ *   q [rows, H, d_k] in_dtype, o [rows, H, d_v] fp32. */
+dl_status dl_readout(dl_state *st, int32_t rows, const int32_t *slot_idx, const void *q,
+                     float *o, void *stream);
+
+/* Synchronise `stream`, copy the device flag word to *flags_out (may be
+ * NULL), clear it, and return DL_ERR_STATE if any bit was set. */
+dl_status dl_state_check(dl_state *st, void *stream, int32_t *flags_out);
+
+/* Message for the latest non-OK status on this thread ("" if none). */
+const char *dl_last_error(void);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t dl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTALOG_H */

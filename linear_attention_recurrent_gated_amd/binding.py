@@ -1,0 +1,276 @@
+"""ctypes binding of ``libdeltalog.so`` (``include/deltalog.h``).
+
+Argument marshalling only: every computation runs in the library's gfx950
+kernels.  The functions below carry the C ABI's names and take raw device
+pointers (ints) and a stream handle; :class:`DecodeState` wraps them for
+torch tensors (torch supplies device memory and streams, nothing else).
+
+If the library is missing this module raises at first use; there is no
+other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdeltalog.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "deltalog.h")
+
+DL_OK, DL_ERR_INVALID, DL_ERR_UNSUPPORTED, DL_ERR_SIZE, DL_ERR_LAUNCH, DL_ERR_STATE = range(6)
+DL_GDN, DL_KDA, DL_RWKV6 = 0, 1, 2
+DL_F32, DL_BF16 = 0, 1
+DL_MERGE_FULL, DL_MERGE_ALL = 0, 1
+DL_FLAG_LOG_FULL, DL_FLAG_LOG_NONEMPTY, DL_FLAG_BAD_SLOT = 1, 2, 4
+
+
+class DlDesc(ctypes.Structure):
+    _fields_ = [("variant", ctypes.c_int32), ("units", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("log_len", ctypes.c_int32), ("in_dtype", ctypes.c_int32)]
+
+
+class DlStatePtrs(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("log_k", ctypes.c_void_p),
+                ("log_v", ctypes.c_void_p), ("log_g", ctypes.c_void_p),
+                ("log_beta", ctypes.c_void_p), ("fill", ctypes.c_void_p),
+                ("flags", ctypes.c_void_p)]
+
+
+class DlError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"deltalog status {status}: {message}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SIGS = {
+    "dl_state_bytes": (ctypes.c_size_t, [ctypes.POINTER(DlDesc)]),
+    "dl_state_alloc": (_I, [ctypes.POINTER(DlDesc), _P, ctypes.c_size_t, _P, ctypes.POINTER(_P)]),
+    "dl_state_free": (_I, [_P]),
+    "dl_state_view": (_I, [_P, ctypes.POINTER(DlStatePtrs)]),
+    "dl_decode_step_eager": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "dl_decode_step_log": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "dl_merge": (_I, [_P, _I, _P, _I, _P]),
+    "dl_merge_replay": (_I, [_P, _I, _P, _I, _P]),
+    "dl_readout": (_I, [_P, _I, _P, _P, _P, _P]),
+    "dl_state_check": (_I, [_P, _P, ctypes.POINTER(_I)]),
+    "dl_last_error": (ctypes.c_char_p, []),
+    "dl_version": (_I, []),
+}
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load the library (once) and declare every entry point's signature."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions include/deltalog.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dl_[a-z_]+)\s*\(", text)))
+
+
+def _check(status: int):
+    if status != DL_OK:
+        raise DlError(status, load().dl_last_error().decode())
+
+
+def dl_last_error() -> str:
+    return load().dl_last_error().decode()
+
+
+def dl_version() -> int:
+    return int(load().dl_version())
+
+
+def dl_state_bytes(desc: DlDesc) -> int:
+    return int(load().dl_state_bytes(ctypes.byref(desc)))
+
+
+def dl_state_alloc(desc: DlDesc, dev_mem: int, nbytes: int, stream: int):
+    out = _P()
+    _check(load().dl_state_alloc(ctypes.byref(desc), dev_mem, nbytes, stream, ctypes.byref(out)))
+    return out
+
+
+def dl_state_free(handle) -> None:
+    _check(load().dl_state_free(handle))
+
+
+def dl_state_view(handle) -> DlStatePtrs:
+    out = DlStatePtrs()
+    _check(load().dl_state_view(handle, ctypes.byref(out)))
+    return out
+
+
+def dl_decode_step_eager(handle, rows, slot_idx, q, k, v, g, beta, o, stream) -> None:
+    _check(load().dl_decode_step_eager(handle, rows, slot_idx, q, k, v, g, beta, o, stream))
+
+
+def dl_decode_step_log(handle, rows, slot_idx, q, k, v, g, beta, o, stream) -> None:
+    _check(load().dl_decode_step_log(handle, rows, slot_idx, q, k, v, g, beta, o, stream))
+
+
+def dl_merge(handle, rows, slot_idx, mode, stream) -> None:
+    _check(load().dl_merge(handle, rows, slot_idx, mode, stream))
+
+
+def dl_merge_replay(handle, rows, slot_idx, mode, stream) -> None:
+    _check(load().dl_merge_replay(handle, rows, slot_idx, mode, stream))
+
+
+def dl_readout(handle, rows, slot_idx, q, o, stream) -> None:
+    _check(load().dl_readout(handle, rows, slot_idx, q, o, stream))
+
+
+def dl_state_check(handle, stream) -> int:
+    """Returns the device flag word (and clears it); raises nothing for set flags."""
+    flags = _I(0)
+    st = load().dl_state_check(handle, stream, ctypes.byref(flags))
+    if st not in (DL_OK, DL_ERR_STATE):
+        _check(st)
+    return int(flags.value)
+
+
+# ---------------------------------------------------------------------------
+# torch convenience layer (memory and streams only)
+# ---------------------------------------------------------------------------
+class DecodeState:
+    """One state block in a torch uint8 device buffer, with tensor views.
+
+    ``base`` ``[units, H, d, d]`` fp32, ``fill`` ``[units, H]`` int32, and the
+    log views ``log_k``/``log_v`` ``[units, H, L, d]`` (input dtype),
+    ``log_g`` ``[units, H, L]`` or ``[units, H, L, d]``, ``log_beta``
+    ``[units, H, L]``.
+    """
+
+    def __init__(self, variant: int, units: int, heads: int, d: int, log_len: int,
+                 dtype: str = "bf16", device="cuda", stream=None):
+        import torch
+
+        self.torch = torch
+        self.variant, self.units, self.heads, self.d, self.L = variant, units, heads, d, log_len
+        self.dtype = dtype
+        self.in_torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.desc = DlDesc(variant, units, heads, d, d, log_len,
+                           DL_BF16 if dtype == "bf16" else DL_F32)
+        nbytes = dl_state_bytes(self.desc)
+        if nbytes == 0:
+            raise DlError(DL_ERR_INVALID, dl_last_error())
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.handle = dl_state_alloc(self.desc, self.buf.data_ptr(), nbytes, self._stream(stream))
+        p = dl_state_view(self.handle)
+        U, H, L = units, heads, log_len
+        self.base = self._view(p.base, torch.float32, (U, H, d, d))
+        self.fill = self._view(p.fill, torch.int32, (U, H))
+        self.flags = self._view(p.flags, torch.int32, (1,))
+        if L > 0:
+            self.log_k = self._view(p.log_k, self.in_torch_dtype, (U, H, L, d))
+            self.log_v = self._view(p.log_v, self.in_torch_dtype, (U, H, L, d))
+            gshape = (U, H, L) if variant == DL_GDN else (U, H, L, d)
+            self.log_g = self._view(p.log_g, torch.float32, gshape)
+            self.log_beta = (self._view(p.log_beta, torch.float32, (U, H, L))
+                             if variant != DL_RWKV6 else None)
+
+    def _view(self, ptr, dtype, shape):
+        torch = self.torch
+        off = int(ptr) - self.buf.data_ptr()
+        n = 1
+        for s in shape:
+            n *= s
+        nbytes = n * torch.empty((), dtype=dtype).element_size()
+        return self.buf[off:off + nbytes].view(dtype).view(shape)
+
+    def _stream(self, stream):
+        if stream is None:
+            return self.torch.cuda.current_stream().cuda_stream
+        return getattr(stream, "cuda_stream", stream)
+
+    def _rows(self, q, slot_idx):
+        rows = q.shape[0]
+        sp = None
+        if slot_idx is not None:
+            assert slot_idx.dtype == self.torch.int32 and slot_idx.is_cuda and slot_idx.is_contiguous()
+            assert slot_idx.shape == (rows,)
+            sp = slot_idx.data_ptr()
+        return rows, sp
+
+    def _check_inputs(self, rows, q, k, v, g, beta):
+        t = self.torch
+        H, d = self.heads, self.d
+        for x in (q, k, v):
+            assert x.dtype == self.in_torch_dtype and x.is_contiguous() and x.shape == (rows, H, d)
+        gshape = (rows, H) if self.variant == DL_GDN else (rows, H, d)
+        assert g.dtype == t.float32 and g.is_contiguous() and tuple(g.shape) == gshape
+        if self.variant != DL_RWKV6:
+            assert beta.dtype == t.float32 and beta.is_contiguous() and beta.shape == (rows, H)
+
+    def _out(self, rows, o):
+        if o is None:
+            o = self.torch.empty((rows, self.heads, self.d), dtype=self.torch.float32,
+                                 device=self.buf.device)
+        assert o.dtype == self.torch.float32 and o.is_contiguous()
+        return o
+
+    def step_eager(self, q, k, v, g, beta=None, o=None, slot_idx=None, stream=None):
+        rows, sp = self._rows(q, slot_idx)
+        self._check_inputs(rows, q, k, v, g, beta)
+        o = self._out(rows, o)
+        dl_decode_step_eager(self.handle, rows, sp, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             g.data_ptr(), None if beta is None else beta.data_ptr(),
+                             o.data_ptr(), self._stream(stream))
+        return o
+
+    def step_log(self, q, k, v, g, beta=None, o=None, slot_idx=None, stream=None):
+        rows, sp = self._rows(q, slot_idx)
+        self._check_inputs(rows, q, k, v, g, beta)
+        o = self._out(rows, o)
+        dl_decode_step_log(self.handle, rows, sp, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           g.data_ptr(), None if beta is None else beta.data_ptr(),
+                           o.data_ptr(), self._stream(stream))
+        return o
+
+    def merge(self, mode: int = DL_MERGE_FULL, rows: int | None = None, slot_idx=None,
+              replay: bool = False, stream=None):
+        if rows is None:
+            rows = self.units if slot_idx is None else slot_idx.shape[0]
+        sp = None if slot_idx is None else slot_idx.data_ptr()
+        fn = dl_merge_replay if replay else dl_merge
+        fn(self.handle, rows, sp, mode, self._stream(stream))
+
+    def readout(self, q, o=None, slot_idx=None, stream=None):
+        rows, sp = self._rows(q, slot_idx)
+        assert q.dtype == self.in_torch_dtype and q.is_contiguous()
+        o = self._out(rows, o)
+        dl_readout(self.handle, rows, sp, q.data_ptr(), o.data_ptr(), self._stream(stream))
+        return o
+
+    def check(self, stream=None) -> int:
+        return dl_state_check(self.handle, self._stream(stream))
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            dl_state_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,328 @@
+// C-ABI entry points (declared in include/deltalog.h): descriptor checks,
+// state-block layout, argument validation and kernel dispatch.  No C++
+// exception crosses this boundary; every failure is a dl_status plus a
+// thread-local message.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "dl_common.hpp"
+
+struct dl_state {
+    dl_desc desc;
+    dl::Params p;
+    void *mem;
+    size_t bytes;
+};
+
+namespace {
+
+thread_local char g_err[512];
+
+dl_status fail(dl_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+dl_status ok() {
+    g_err[0] = '\0';
+    return DL_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct Layout {
+    size_t off_flags, off_fill, off_base, off_k, off_v, off_g, off_b, total;
+};
+
+dl_status check_desc(const dl_desc *d) {
+    if (!d)
+        return fail(DL_ERR_INVALID, "descriptor is NULL");
+    if (d->variant < DL_GDN || d->variant > DL_RWKV6)
+        return fail(DL_ERR_INVALID, "unknown variant %d", d->variant);
+    if (d->units < 1 || d->heads < 1)
+        return fail(DL_ERR_INVALID, "units (%d) and heads (%d) must be >= 1", d->units, d->heads);
+    if (d->in_dtype != DL_F32 && d->in_dtype != DL_BF16)
+        return fail(DL_ERR_INVALID, "unknown input dtype %d", d->in_dtype);
+    if (d->log_len < 0)
+        return fail(DL_ERR_INVALID, "log_len must be >= 0, got %d", d->log_len);
+    if (d->d_k != d->d_v)
+        return fail(DL_ERR_UNSUPPORTED, "d_k (%d) != d_v (%d) is not built", d->d_k, d->d_v);
+    if (d->d_k != 64 && d->d_k != 128)
+        return fail(DL_ERR_UNSUPPORTED, "d = %d is not built (64 or 128)", d->d_k);
+    if (d->log_len > 64)
+        return fail(DL_ERR_UNSUPPORTED, "log_len %d > 64 is not built", d->log_len);
+    const size_t pairs = (size_t)d->units * (size_t)d->heads;
+    if (pairs > (size_t)0x7fffffff)
+        return fail(DL_ERR_INVALID, "units * heads too large");
+    return DL_OK;
+}
+
+Layout layout_of(const dl_desc &d) {
+    Layout l;
+    const size_t pairs = (size_t)d.units * d.heads;
+    const size_t es = d.in_dtype == DL_BF16 ? 2 : 4;
+    const size_t L = d.log_len;
+    const size_t gch = d.variant == DL_GDN ? 1 : d.d_k;
+    size_t off = 0;
+    l.off_flags = off;
+    off = align256(off + 256);
+    l.off_fill = off;
+    off = align256(off + pairs * 4);
+    l.off_base = off;
+    off = align256(off + pairs * d.d_v * d.d_k * 4);
+    l.off_k = off;
+    off = align256(off + pairs * L * d.d_k * es);
+    l.off_v = off;
+    off = align256(off + pairs * L * d.d_v * es);
+    l.off_g = off;
+    off = align256(off + pairs * L * gch * 4);
+    l.off_b = off;
+    off = align256(off + (d.variant == DL_RWKV6 ? 0 : pairs * L * 4));
+    l.total = off;
+    return l;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+dl_status check_rows(const dl_state *st, int32_t rows, const int32_t *slot_idx) {
+    if (!st)
+        return fail(DL_ERR_INVALID, "state handle is NULL");
+    if (rows < 0)
+        return fail(DL_ERR_INVALID, "rows must be >= 0, got %d", rows);
+    if (!slot_idx && rows > st->desc.units)
+        return fail(DL_ERR_INVALID, "rows (%d) > units (%d) without slot_idx", rows, st->desc.units);
+    if (slot_idx && !aligned(slot_idx, 4))
+        return fail(DL_ERR_INVALID, "slot_idx must be 4-byte aligned");
+    if ((size_t)rows * st->desc.heads > (size_t)0x7fffffff)
+        return fail(DL_ERR_INVALID, "rows * heads too large for one launch");
+    return DL_OK;
+}
+
+dl_status check_step_args(const dl_state *st, int32_t rows, const int32_t *slot_idx,
+                          const void *q, const void *k, const void *v, const float *g,
+                          const float *beta, const float *o) {
+    dl_status s = check_rows(st, rows, slot_idx);
+    if (s != DL_OK)
+        return s;
+    if (!q || !k || !v || !g || !o)
+        return fail(DL_ERR_INVALID, "q, k, v, g and o must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(DL_ERR_INVALID, "q, k, v and o must be 16-byte aligned");
+    if (!aligned(g, st->desc.variant == DL_GDN ? 4 : 16))
+        return fail(DL_ERR_INVALID, "g must be %d-byte aligned",
+                    st->desc.variant == DL_GDN ? 4 : 16);
+    if (st->desc.variant != DL_RWKV6) {
+        if (!beta)
+            return fail(DL_ERR_INVALID, "beta is required for the delta-rule variants");
+        if (!aligned(beta, 4))
+            return fail(DL_ERR_INVALID, "beta must be 4-byte aligned");
+    }
+    return DL_OK;
+}
+
+// The step/readout kernels stage the key side of the log (keys, decays,
+// betas) in LDS; the request must fit the current device's per-workgroup
+// LDS (160 KiB on gfx950).
+dl_status check_lds(const dl_state *st) {
+    const int es = st->desc.in_dtype == DL_BF16 ? 2 : 4;
+    const dl::LdsPlan lp = dl::lds_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len,
+                                        st->desc.log_len, false);
+    if (lp.bytes <= 65536)
+        return DL_OK;
+    int dev = 0, max_lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+        return fail(DL_ERR_LAUNCH, "cannot query the device's LDS size");
+    if (lp.bytes > max_lds)
+        return fail(DL_ERR_UNSUPPORTED, "log of %d entries needs %d bytes of LDS (device limit %d)",
+                    st->desc.log_len, lp.bytes, max_lds);
+    return DL_OK;
+}
+
+dl_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess)
+        return fail(DL_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dl_state_bytes(const dl_desc *desc) {
+    if (check_desc(desc) != DL_OK)
+        return 0;
+    return layout_of(*desc).total;
+}
+
+dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void *stream,
+                         dl_state **out) {
+    dl_status s = check_desc(desc);
+    if (s != DL_OK)
+        return s;
+    if (!out)
+        return fail(DL_ERR_INVALID, "out is NULL");
+    *out = nullptr;
+    if (!dev_mem)
+        return fail(DL_ERR_INVALID, "device memory is NULL");
+    if (!aligned(dev_mem, 256))
+        return fail(DL_ERR_INVALID, "device memory must be 256-byte aligned");
+    const Layout l = layout_of(*desc);
+    if (bytes < l.total)
+        return fail(DL_ERR_SIZE, "state block needs %zu bytes, got %zu", l.total, bytes);
+    dl_state *st = new (std::nothrow) dl_state;
+    if (!st)
+        return fail(DL_ERR_INVALID, "out of host memory");
+    st->desc = *desc;
+    st->mem = dev_mem;
+    st->bytes = bytes;
+    char *m = static_cast<char *>(dev_mem);
+    dl::Params &p = st->p;
+    p.variant = desc->variant;
+    p.units = desc->units;
+    p.heads = desc->heads;
+    p.D = desc->d_k;
+    p.L = desc->log_len;
+    p.dtype = desc->in_dtype;
+    p.flags = reinterpret_cast<int *>(m + l.off_flags);
+    p.fill = reinterpret_cast<int *>(m + l.off_fill);
+    p.base = reinterpret_cast<float *>(m + l.off_base);
+    const bool has_log = desc->log_len > 0;
+    p.log_k = has_log ? m + l.off_k : nullptr;
+    p.log_v = has_log ? m + l.off_v : nullptr;
+    p.log_g = has_log ? reinterpret_cast<float *>(m + l.off_g) : nullptr;
+    p.log_beta = (has_log && desc->variant != DL_RWKV6) ? reinterpret_cast<float *>(m + l.off_b)
+                                                        : nullptr;
+    const hipError_t e = dl::launch_zero(dev_mem, l.total, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        delete st;
+        return fail(DL_ERR_LAUNCH, "zeroing the state block: %s", hipGetErrorString(e));
+    }
+    *out = st;
+    return ok();
+}
+
+dl_status dl_state_free(dl_state *st) {
+    delete st;
+    return ok();
+}
+
+dl_status dl_state_view(const dl_state *st, dl_state_ptrs *out) {
+    if (!st || !out)
+        return fail(DL_ERR_INVALID, "state and out must be non-NULL");
+    out->base = st->p.base;
+    out->log_k = st->p.log_k;
+    out->log_v = st->p.log_v;
+    out->log_g = st->p.log_g;
+    out->log_beta = st->p.log_beta;
+    out->fill = st->p.fill;
+    out->flags = st->p.flags;
+    return ok();
+}
+
+dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                               const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float *o, void *stream) {
+    dl_status s = check_step_args(st, rows, slot_idx, q, k, v, g, beta, o);
+    if (s != DL_OK)
+        return s;
+    if (rows == 0)
+        return ok();
+    return launched(dl::launch_eager(st->p, rows, slot_idx, q, k, v, g, beta, o,
+                                     static_cast<hipStream_t>(stream)),
+                    "eager step launch");
+}
+
+dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                             const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *o, void *stream) {
+    dl_status s = check_step_args(st, rows, slot_idx, q, k, v, g, beta, o);
+    if (s != DL_OK)
+        return s;
+    if (st->desc.log_len < 1)
+        return fail(DL_ERR_INVALID, "this state has no log (log_len = 0)");
+    s = check_lds(st);
+    if (s != DL_OK)
+        return s;
+    if (rows == 0)
+        return ok();
+    return launched(dl::launch_log_step(st->p, rows, slot_idx, q, k, v, g, beta, o,
+                                        static_cast<hipStream_t>(stream)),
+                    "log step launch");
+}
+
+static dl_status merge_common(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
+                              void *stream, bool wy) {
+    dl_status s = check_rows(st, rows, slot_idx);
+    if (s != DL_OK)
+        return s;
+    if (mode != DL_MERGE_FULL && mode != DL_MERGE_ALL)
+        return fail(DL_ERR_INVALID, "unknown merge mode %d", mode);
+    if (st->desc.log_len < 1 || rows == 0)
+        return ok();
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const hipError_t e = wy ? dl::launch_merge_wy(st->p, rows, slot_idx, mode, hs)
+                            : dl::launch_merge_replay(st->p, rows, slot_idx, mode, hs);
+    return launched(e, "merge launch");
+}
+
+dl_status dl_merge(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
+                   void *stream) {
+    return merge_common(st, rows, slot_idx, mode, stream, true);
+}
+
+dl_status dl_merge_replay(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
+                          void *stream) {
+    return merge_common(st, rows, slot_idx, mode, stream, false);
+}
+
+dl_status dl_readout(dl_state *st, int32_t rows, const int32_t *slot_idx, const void *q,
+                     float *o, void *stream) {
+    dl_status s = check_rows(st, rows, slot_idx);
+    if (s != DL_OK)
+        return s;
+    if (!q || !o)
+        return fail(DL_ERR_INVALID, "q and o must be non-NULL");
+    if (!aligned(q, 16) || !aligned(o, 16))
+        return fail(DL_ERR_INVALID, "q and o must be 16-byte aligned");
+    s = check_lds(st);
+    if (s != DL_OK)
+        return s;
+    if (rows == 0)
+        return ok();
+    return launched(dl::launch_readout(st->p, rows, slot_idx, q, o, static_cast<hipStream_t>(stream)),
+                    "readout launch");
+}
+
+dl_status dl_state_check(dl_state *st, void *stream, int32_t *flags_out) {
+    if (!st)
+        return fail(DL_ERR_INVALID, "state handle is NULL");
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    int32_t h = 0;
+    hipError_t e = hipMemcpyAsync(&h, st->p.flags, sizeof(int32_t), hipMemcpyDeviceToHost, hs);
+    if (e == hipSuccess)
+        e = hipStreamSynchronize(hs);
+    if (e != hipSuccess)
+        return fail(DL_ERR_LAUNCH, "reading device flags: %s", hipGetErrorString(e));
+    if (flags_out)
+        *flags_out = h;
+    if (h != 0) {
+        e = dl::launch_zero(st->p.flags, 256, hs);
+        if (e != hipSuccess)
+            return fail(DL_ERR_LAUNCH, "clearing device flags: %s", hipGetErrorString(e));
+        return fail(DL_ERR_STATE, "device flags 0x%x (1: log full, 2: eager on non-empty log, 4: bad slot)", h);
+    }
+    return ok();
+}
+
+const char *dl_last_error(void) { return g_err; }
+
+int32_t dl_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,384 @@
+// Merge kernels for gfx950: materialise base + log into a new base and empty
+// the log (the Merge Phase of the DeltaLog page, "DeltaLog: Deferred
+// Materialization of Recurrent States for Linear Attention Decoding",
+// Technical Summary, Core Mechanism).
+//
+// merge_wy_kernel -- the logged transforms folded in WY/UT form, the block
+// form the CARVE page (abstract: WY-form triangular chunk solver) and Gated
+// DeltaNet-2 (chunkwise WY algorithm) use.  For a chunk of C = 16 entries
+// with chunk-local cumulative log-decay Lam_j (per key channel):
+//   Kt_j = k_j exp(Lam_j)                         (decayed keys)
+//   W    = S Kt^T                                 (d_v x C, MFMA)
+//   M_ij = beta_j sum_c k_i k_j exp(Lam_j - Lam_i)   for i < j
+//   Kh_j = k_j exp(Lam_C - Lam_j)
+//   Y    = diag(beta) (I + M)^{-1} Kh             (C x d_k, back substitution)
+//   S'   = S diag(exp(Lam_C)) + (V^T - W) Y       (MFMA)
+// (additive variant: S' = S diag(exp(Lam_C)) + V^T Kh).  This is the
+// recurrence unrolled over the chunk: with u_j = beta_j (v_j - S_{j-1}
+// diag(alpha_j) k_j), S_C = S_0 diag(exp Lam_C) + sum_j u_j Kh_j^T and the
+// u_j solve U (I + M) = (V^T - W) diag(beta).  Chunks run one after the
+// other; decays never exceed 1 inside a chunk, so nothing overflows.
+//
+// The base stays in registers for the whole merge, in the MFMA operand
+// layout of v_mfma_f32_16x16x4_f32 (lane l: row l % 16 of a 16-row value
+// tile, column sub-block l / 16): those registers are the B operand of
+// W^T = Kt S^T and, read as 16 x 16 output tiles, the accumulators of the
+// update S'^T = diag(exp Lam_C) S^T + Y^T Z^T -- no transposes, no reloads.
+//
+// merge_replay_kernel -- the same result by replaying the logged steps one
+// by one on the vector ALUs (cross-check).
+#include "dl_common.hpp"
+
+namespace dl {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bool resolve_merge_pair(const Params &P, const int *slot_idx, int mode,
+                                                   size_t &pair, int &n) {
+    const int H = P.heads;
+    const int pr = blockIdx.x;
+    const int r = pr / H, h = pr - r * H;
+    const int unit = slot_idx ? slot_idx[r] : r;
+    if (unit < 0 || unit >= P.units) {
+        reject_row(P, nullptr, P.D, DL_FLAG_BAD_SLOT);
+        return false;
+    }
+    pair = (size_t)unit * H + h;
+    n = P.fill[pair];
+    if (n <= 0 || n > P.L)
+        return false;
+    if (mode == DL_MERGE_FULL && n != P.L)
+        return false;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// replay merge (VALU)
+// ---------------------------------------------------------------------------
+template <int V, int D, typename T>
+__global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *__restrict__ slot_idx,
+                                                           int mode) {
+    using SH = Shape<D>;
+    extern __shared__ __align__(16) unsigned char smem[];
+    size_t pair;
+    int n;
+    if (!resolve_merge_pair(P, slot_idx, mode, pair, n))
+        return;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = lane >> 3, s = lane & 7;
+    const int CH = P.L < 32 ? P.L : 32;
+    const LdsPlan lp = lds_plan(V, D, (int)sizeof(T), CH, P.L, true);
+
+    float *Sp = P.base + pair * D * D;
+    float4 st[SH::ITER][SH::NCH];
+#pragma unroll
+    for (int it = 0; it < SH::ITER; ++it) {
+        const int row = wave * SH::RPW + it * 8 + grp;
+#pragma unroll
+        for (int m = 0; m < SH::NCH; ++m)
+            st[it][m] = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + col_of(s, m, 0));
+    }
+    const unsigned char *sk = smem + lp.off_k;
+    const float *sa = reinterpret_cast<const float *>(smem + lp.off_a);
+    const float *sb = reinterpret_cast<const float *>(smem + lp.off_b);
+
+    for (int j0 = 0; j0 < n; j0 += CH) {
+        const int cnt = (n - j0) < CH ? (n - j0) : CH;
+        __syncthreads();
+        stage_entries<V, D, T, true>(P, pair, j0, cnt, smem, lp);
+        __syncthreads();
+        for (int j = 0; j < cnt; ++j) {
+            float kj[SH::FPL], ak[SH::FPL], aj[SH::FPL];
+            float a_s = 1.f;
+#pragma unroll
+            for (int m = 0; m < SH::NCH; ++m) {
+                f4_to(kj + 4 * m, lds_load4<T>(sk, j * D + col_of(s, m, 0)));
+                if constexpr (V != GDN)
+                    f4_to(aj + 4 * m, *reinterpret_cast<const float4 *>(sa + j * D + col_of(s, m, 0)));
+            }
+            if constexpr (V == GDN)
+                a_s = sa[j];
+#pragma unroll
+            for (int f = 0; f < SH::FPL; ++f)
+                ak[f] = (V == GDN) ? kj[f] : aj[f] * kj[f];
+            const float bj = (V == RWKV6) ? 1.f : sb[j];
+            const unsigned char *vrow = smem + lp.off_v + j * lp.v_stride;
+#pragma unroll
+            for (int it = 0; it < SH::ITER; ++it) {
+                const int row = wave * SH::RPW + it * 8 + grp;
+                float u = 0.f;
+                if constexpr (V != RWKV6) {
+#pragma unroll
+                    for (int m = 0; m < SH::NCH; ++m)
+                        u += st[it][m].x * ak[4 * m] + st[it][m].y * ak[4 * m + 1] +
+                             st[it][m].z * ak[4 * m + 2] + st[it][m].w * ak[4 * m + 3];
+                    u = sum8(u);
+                    if constexpr (V == GDN)
+                        u *= a_s;
+                }
+                const float vj = Elem<T>::load1(reinterpret_cast<const T *>(vrow) + row);
+                const float d = (V == RWKV6) ? vj : bj * (vj - u);
+#pragma unroll
+                for (int m = 0; m < SH::NCH; ++m) {
+                    float sv[4] = {st[it][m].x, st[it][m].y, st[it][m].z, st[it][m].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int f = 4 * m + e;
+                        sv[e] = ((V == GDN) ? a_s * sv[e] : sv[e] * aj[f]) + d * kj[f];
+                    }
+                    st[it][m] = make_float4(sv[0], sv[1], sv[2], sv[3]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int it = 0; it < SH::ITER; ++it) {
+        const int row = wave * SH::RPW + it * 8 + grp;
+#pragma unroll
+        for (int m = 0; m < SH::NCH; ++m)
+            *reinterpret_cast<float4 *>(Sp + (size_t)row * D + col_of(s, m, 0)) = st[it][m];
+    }
+    if (tid == 0)
+        P.fill[pair] = 0;
+}
+
+// ---------------------------------------------------------------------------
+// WY merge (MFMA)
+// ---------------------------------------------------------------------------
+template <int V, int D, typename T>
+__global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__restrict__ slot_idx,
+                                                       int mode) {
+    constexpr int C = 16;               // entries per WY chunk
+    constexpr int NIT = D / 64;         // 16-row value tiles per wave
+    constexpr int NM = D / 16;          // 16-column blocks
+    constexpr int KS = D + 4;           // padded LDS row stride (floats)
+    __shared__ __align__(16) float sKt[C * KS];   // k_j exp(Lam_j)
+    __shared__ __align__(16) float sY[C * KS];    // rows of diag(beta)(I+M)^{-1} Kh
+    __shared__ float sLam[C * D];                 // chunk-local cumulative log-decay
+    __shared__ float sK[C * D];                   // keys, fp32
+    __shared__ float sM[C * C];                   // beta_j G_ij, i < j
+    __shared__ float sB[C];
+    __shared__ __align__(16) float sELC[D];       // exp(Lam_C) per key channel
+
+    size_t pair;
+    int n;
+    if (!resolve_merge_pair(P, slot_idx, mode, pair, n))
+        return;
+    const int L = P.L;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, kg = lane >> 4;
+    float *Sp = P.base + pair * D * D;
+    const T *Kl = static_cast<const T *>(P.log_k) + pair * L * D;
+    const T *Vl = static_cast<const T *>(P.log_v) + pair * L * D;
+    const float *Gl = P.log_g + pair * L * ((V == GDN) ? 1 : D);
+    const float *Bl = P.log_beta + pair * L;
+
+    // base rows in MFMA operand layout: st[it][m].e = S[16 (wave NIT + it) + li][4 kg + 16 m + e]
+    floatx4 st[NIT][NM];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int row = 16 * (wave * NIT + it) + li;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const float4 x = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + 4 * kg + 16 * m);
+            st[it][m] = floatx4{x.x, x.y, x.z, x.w};
+        }
+    }
+
+    for (int j0 = 0; j0 < n; j0 += C) {
+        const int cnt = (n - j0) < C ? (n - j0) : C;
+        __syncthreads();   // previous chunk's LDS reads are done
+
+        // ---- stage: thread c walks its key channel through the chunk
+        float lam_r[C], kr[C];
+        if (tid < D) {
+            const int c = tid;
+            float lam = 0.f;
+#pragma unroll
+            for (int j = 0; j < C; ++j) {
+                float kk = 0.f;
+                if (j < cnt) {
+                    const int e = j0 + j;
+                    lam += (V == GDN) ? Gl[e] : Gl[(size_t)e * D + c];
+                    kk = Elem<T>::load1(Kl + (size_t)e * D + c);
+                }
+                lam_r[j] = lam;
+                kr[j] = kk;
+                sKt[j * KS + c] = kk * expf(lam);
+                sLam[j * D + c] = lam;
+                sK[j * D + c] = kk;
+            }
+            sELC[c] = expf(lam);
+        }
+        if (tid < C)
+            sB[tid] = (V != RWKV6 && tid < cnt) ? Bl[j0 + tid] : 0.f;
+        __syncthreads();
+
+        // ---- Gram with pairwise decay: two lanes per pair (i < j), halves of the channels
+        if constexpr (V != RWKV6) {
+            const int p = tid >> 1, half = tid & 1;
+            int i = 0, j = 1;
+            bool inpair = p < C * (C - 1) / 2;
+            if (inpair) {
+                int base = 0;
+                while (base + j <= p) {
+                    base += j;
+                    ++j;
+                }
+                i = p - base;
+            }
+            const bool valid = inpair && j < cnt;
+            float gsum = 0.f;
+            if (valid) {
+                const int c0 = half * (D / 2);
+                for (int c = c0; c < c0 + D / 2; ++c) {
+                    const float kk = sK[i * D + c] * sK[j * D + c];
+                    gsum += (V == GDN) ? kk : kk * expf(sLam[j * D + c] - sLam[i * D + c]);
+                }
+            }
+            gsum += dpp_mov<0xB1>(gsum);   // add the other half (adjacent lane)
+            if (V == GDN && valid)
+                gsum *= expf(sLam[j * D] - sLam[i * D]);
+            if (inpair && half == 0)
+                sM[i * C + j] = valid ? sB[j] * gsum : 0.f;
+        }
+        __syncthreads();
+
+        // ---- Y = diag(beta) (I + M)^{-1} Kh by back substitution, one channel per thread
+        if (tid < D) {
+            const int c = tid;
+            const float lamC = lam_r[C - 1];
+            float x[C];
+#pragma unroll
+            for (int j = C - 1; j >= 0; --j) {
+                float kh = (j < cnt) ? kr[j] * expf(lamC - lam_r[j]) : 0.f;
+                if constexpr (V != RWKV6) {
+#pragma unroll
+                    for (int m = j + 1; m < C; ++m)
+                        kh -= sM[j * C + m] * x[m];
+                    x[j] = kh;
+                    sY[j * KS + c] = sB[j] * kh;
+                } else {
+                    sY[j * KS + c] = kh;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- W^T = Kt S^T (MFMA), Z^T = V^T - W^T in the output layout:
+        //      z[it][r] = Z[row 16 (wave NIT + it) + li][entry 4 kg + r]
+        floatx4 z[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (V != RWKV6) {
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    const float4 a = *reinterpret_cast<const float4 *>(&sKt[li * KS + 4 * kg + 16 * m]);
+                    acc = mfma16x16x4(a.x, st[it][m][0], acc);
+                    acc = mfma16x16x4(a.y, st[it][m][1], acc);
+                    acc = mfma16x16x4(a.z, st[it][m][2], acc);
+                    acc = mfma16x16x4(a.w, st[it][m][3], acc);
+                }
+            }
+            const int row = 16 * (wave * NIT + it) + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 4 * kg + r;
+                const float vv = (j < cnt) ? Elem<T>::load1(Vl + (size_t)(j0 + j) * D + row) : 0.f;
+                z[it][r] = vv - acc[r];
+            }
+        }
+
+        // ---- S'^T = diag(exp Lam_C) S^T + Y^T Z^T (MFMA, accumulating in place)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const float4 el = *reinterpret_cast<const float4 *>(&sELC[4 * kg + 16 * m]);
+            float a[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                a[r] = sY[(4 * kg + r) * KS + 16 * m + li];
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) {
+                floatx4 acc = st[it][m];
+                acc[0] *= el.x;
+                acc[1] *= el.y;
+                acc[2] *= el.z;
+                acc[3] *= el.w;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc = mfma16x16x4(a[r], z[it][r], acc);
+                st[it][m] = acc;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+        const int row = 16 * (wave * NIT + it) + li;
+#pragma unroll
+        for (int m = 0; m < NM; ++m)
+            *reinterpret_cast<float4 *>(Sp + (size_t)row * D + 4 * kg + 16 * m) =
+                make_float4(st[it][m][0], st[it][m][1], st[it][m][2], st[it][m][3]);
+    }
+    if (tid == 0)
+        P.fill[pair] = 0;
+}
+
+// ---------------------------------------------------------------------------
+#define DL_DISPATCH_M(P, FN, ...)                                                        \
+    do {                                                                                 \
+        const bool bf = (P).dtype == DL_BF16;                                            \
+        if ((P).D == 128) {                                                              \
+            if (bf) {                                                                    \
+                if ((P).variant == DL_GDN) return FN<GDN, 128, uint16_t>(__VA_ARGS__);   \
+                if ((P).variant == DL_KDA) return FN<KDA, 128, uint16_t>(__VA_ARGS__);   \
+                return FN<RWKV6, 128, uint16_t>(__VA_ARGS__);                            \
+            }                                                                            \
+            if ((P).variant == DL_GDN) return FN<GDN, 128, float>(__VA_ARGS__);          \
+            if ((P).variant == DL_KDA) return FN<KDA, 128, float>(__VA_ARGS__);          \
+            return FN<RWKV6, 128, float>(__VA_ARGS__);                                   \
+        }                                                                                \
+        if (bf) {                                                                        \
+            if ((P).variant == DL_GDN) return FN<GDN, 64, uint16_t>(__VA_ARGS__);        \
+            if ((P).variant == DL_KDA) return FN<KDA, 64, uint16_t>(__VA_ARGS__);        \
+            return FN<RWKV6, 64, uint16_t>(__VA_ARGS__);                                 \
+        }                                                                                \
+        if ((P).variant == DL_GDN) return FN<GDN, 64, float>(__VA_ARGS__);               \
+        if ((P).variant == DL_KDA) return FN<KDA, 64, float>(__VA_ARGS__);               \
+        return FN<RWKV6, 64, float>(__VA_ARGS__);                                        \
+    } while (0)
+
+template <int V, int D, typename T>
+static hipError_t replay_t(const Params &P, int rows, const int *slot_idx, int mode,
+                           hipStream_t stream) {
+    const int CH = P.L < 32 ? P.L : 32;
+    const LdsPlan lp = lds_plan(V, D, (int)sizeof(T), CH, P.L, true);
+    hipLaunchKernelGGL((merge_replay_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), lp.bytes,
+                       stream, P, slot_idx, mode);
+    return hipGetLastError();
+}
+
+template <int V, int D, typename T>
+static hipError_t wy_t(const Params &P, int rows, const int *slot_idx, int mode,
+                       hipStream_t stream) {
+    hipLaunchKernelGGL((merge_wy_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), 0, stream, P,
+                       slot_idx, mode);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge_replay(const Params &P, int rows, const int *slot_idx, int mode,
+                               hipStream_t stream) {
+    DL_DISPATCH_M(P, replay_t, P, rows, slot_idx, mode, stream);
+}
+
+hipError_t launch_merge_wy(const Params &P, int rows, const int *slot_idx, int mode,
+                           hipStream_t stream) {
+    DL_DISPATCH_M(P, wy_t, P, rows, slot_idx, mode, stream);
+}
+
+}  // namespace dl

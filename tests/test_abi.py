@@ -1,0 +1,112 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, sizes state blocks as documented and rejects bad arguments before
+touching the GPU.  No kernel runs here."""
+from __future__ import annotations
+
+import ctypes
+import subprocess
+
+import pytest
+
+from linear_attention_recurrent_gated_amd import binding as B
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = B.header_functions()
+    assert len(declared) >= 12
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [f for f in declared if f not in exported]
+    assert not missing, missing
+    for name in declared:
+        assert hasattr(lib, name)
+    assert set(B._SIGS) == set(declared)
+
+
+def test_library_is_gfx950_only():
+    """The library embeds device code for gfx950 and for no other target."""
+    out = subprocess.run(["strings", B.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "amdgcn-amd-amdhsa--gfx950" in out
+    for other in ("gfx942", "gfx90a", "gfx908", "gfx1100", "sm_"):
+        assert f"amdhsa--{other}" not in out
+
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+def _expected_bytes(variant, units, heads, d, L, es):
+    pairs = units * heads
+    total = _align(256) + _align(pairs * 4) + _align(pairs * d * d * 4)
+    total += _align(pairs * L * d * es) * 2
+    total += _align(pairs * L * (1 if variant == B.DL_GDN else d) * 4)
+    total += _align(0 if variant == B.DL_RWKV6 else pairs * L * 4)
+    return total
+
+
+@pytest.mark.parametrize("variant", [B.DL_GDN, B.DL_KDA, B.DL_RWKV6])
+@pytest.mark.parametrize("d,L,dt,es", [(128, 16, B.DL_BF16, 2), (64, 32, B.DL_F32, 4),
+                                       (128, 0, B.DL_BF16, 2), (64, 64, B.DL_BF16, 2)])
+def test_state_bytes(variant, d, L, dt, es):
+    desc = B.DlDesc(variant, 7, 3, d, d, L, dt)
+    assert B.dl_state_bytes(desc) == _expected_bytes(variant, 7, 3, d, L, es)
+
+
+def test_state_bytes_full_size_configs():
+    # 64 x 32 heads of 128 x 128 fp32 = 128 MiB of state plus the log
+    desc = B.DlDesc(B.DL_GDN, 64, 32, 128, 128, 16, B.DL_BF16)
+    assert B.dl_state_bytes(desc) >= 128 * 2**20
+    desc = B.DlDesc(B.DL_GDN, 256, 32, 128, 128, 32, B.DL_BF16)
+    assert B.dl_state_bytes(desc) >= 512 * 2**20
+
+
+@pytest.mark.parametrize("fields,code", [
+    ((3, 4, 2, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),      # unknown variant
+    ((0, 0, 2, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),      # no units
+    ((0, 4, 0, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),      # no heads
+    ((0, 4, 2, 128, 128, 8, 7), B.DL_ERR_INVALID),              # unknown dtype
+    ((0, 4, 2, 128, 128, -1, B.DL_BF16), B.DL_ERR_INVALID),     # negative L
+    ((0, 4, 2, 128, 64, 8, B.DL_BF16), B.DL_ERR_UNSUPPORTED),   # d_k != d_v
+    ((0, 4, 2, 96, 96, 8, B.DL_BF16), B.DL_ERR_UNSUPPORTED),    # d not built
+    ((0, 4, 2, 128, 128, 65, B.DL_BF16), B.DL_ERR_UNSUPPORTED), # L too long
+])
+def test_bad_descriptors(lib, fields, code):
+    desc = B.DlDesc(*fields)
+    assert B.dl_state_bytes(desc) == 0
+    out = ctypes.c_void_p()
+    st = lib.dl_state_alloc(ctypes.byref(desc), ctypes.c_void_p(256), 1 << 30, None, ctypes.byref(out))
+    assert st == code
+    assert out.value is None
+    assert B.dl_last_error()
+
+
+def test_alloc_checks_memory_before_launching(lib):
+    desc = B.DlDesc(B.DL_GDN, 4, 2, 128, 128, 8, B.DL_BF16)
+    need = B.dl_state_bytes(desc)
+    out = ctypes.c_void_p()
+    assert lib.dl_state_alloc(ctypes.byref(desc), None, need, None, ctypes.byref(out)) == B.DL_ERR_INVALID
+    assert lib.dl_state_alloc(ctypes.byref(desc), ctypes.c_void_p(4096 + 8), need, None,
+                              ctypes.byref(out)) == B.DL_ERR_INVALID        # misaligned
+    assert lib.dl_state_alloc(ctypes.byref(desc), ctypes.c_void_p(4096), need - 1, None,
+                              ctypes.byref(out)) == B.DL_ERR_SIZE
+    assert "needs" in B.dl_last_error()
+    assert lib.dl_state_alloc(ctypes.byref(desc), ctypes.c_void_p(4096), need, None, None) == B.DL_ERR_INVALID
+
+
+def test_null_handle_is_rejected(lib):
+    p = ctypes.c_void_p(4096)
+    assert lib.dl_decode_step_eager(None, 1, None, p, p, p, p, p, p, None) == B.DL_ERR_INVALID
+    assert lib.dl_decode_step_log(None, 1, None, p, p, p, p, p, p, None) == B.DL_ERR_INVALID
+    assert lib.dl_merge(None, 1, None, 0, None) == B.DL_ERR_INVALID
+    assert lib.dl_merge_replay(None, 1, None, 0, None) == B.DL_ERR_INVALID
+    assert lib.dl_readout(None, 1, None, p, p, None) == B.DL_ERR_INVALID
+    assert lib.dl_state_check(None, None, None) == B.DL_ERR_INVALID
+    assert lib.dl_state_view(None, None) == B.DL_ERR_INVALID
+    assert lib.dl_state_free(None) == B.DL_OK
+    assert B.dl_version() == 100

@@ -1,0 +1,201 @@
+"""GPU edge cases: the log schedule bit for bit, readout, device flags,
+slot mapping, argument checks that need a live state."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrent_gated_amd import binding as B
+from linear_attention_recurrent_gated_amd import workloads as W
+
+from gpu_harness import TOL, log, per_pair_error, run_case, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(wl, tau, rows=None):
+    s = W.draw_step(wl, tau)
+    sl = slice(None) if rows is None else rows
+    q, k, v = (to_torch(x[sl], wl.dtype) for x in (s.q, s.k, s.v))
+    g = torch.from_numpy(np.ascontiguousarray(s.g[sl])).cuda()
+    beta = None if s.beta is None else torch.from_numpy(np.ascontiguousarray(s.beta[sl])).cuda()
+    return s, (q, k, v, g, beta)
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32).cpu().numpy()
+
+
+@pytest.mark.parametrize("wl,L", [
+    (W.GDN_LARGE.scaled(batch=5, layers=1, heads=2, steps=14), 4),
+    (W.KDA_SWEEP.scaled(batch=3, heads=2, steps=11, ragged=True), 3),
+    (W.RWKV6_ADD.scaled(batch=3, heads=2, steps=9, ragged=True), 5),
+])
+def test_schedule_and_payload_bit_exact(wl, L):
+    """After every step: fill == (tokens so far) mod L for every head, and the
+    slot written holds bit copies of that step's k, v, g, beta."""
+    first = W.first_active_step(wl, L)
+    log(f"case schedule {wl.name} L={L} offsets={L - 1 - first}")
+
+    def on_step(tau, states):
+        st = states["log"][0]
+        s = W.draw_step(wl, tau)
+        fill = st.fill.cpu().numpy()
+        for b in range(wl.batch):
+            m = tau - first[b] + 1                      # tokens this sequence has taken
+            expect = max(m, 0) % L
+            assert np.all(fill[b] == expect), (tau, b, fill[b], expect)
+            if m <= 0:
+                continue
+            slot = (m - 1) % L
+            assert np.array_equal(_bits(st.log_k[b, :, slot]), _bits(to_torch(s.k[b], wl.dtype)))
+            assert np.array_equal(_bits(st.log_v[b, :, slot]), _bits(to_torch(s.v[b], wl.dtype)))
+            assert np.array_equal(st.log_g[b, :, slot].cpu().numpy(), s.g[b])
+            if s.beta is not None:
+                assert np.array_equal(st.log_beta[b, :, slot].cpu().numpy(), s.beta[b])
+
+    run_case(wl, L, ("log",), merge_every_step=True, run_oracle=False, on_step=on_step)
+
+
+@pytest.mark.parametrize("wl", [W.GDN_HYBRID.scaled(batch=2, heads=3, steps=20),
+                                W.KDA_SWEEP.scaled(batch=2, heads=3, steps=20),
+                                W.RWKV6_ADD.scaled(batch=2, heads=3, steps=20)],
+                         ids=["gdn", "kda", "rwkv6"])
+def test_readout_matches_oracle(wl):
+    """dl_readout returns S_t q for a fresh q, mid-log and after merges, and changes nothing."""
+    L = 6
+    H, d = wl.heads, wl.d_k
+    P = wl.batch * H
+    log(f"case readout {wl.name}")
+    st = B.DecodeState(wl.variant, wl.batch, H, d, L, wl.dtype)
+    eg = B.DecodeState(wl.variant, wl.batch, H, d, 0, wl.dtype)
+    S0 = W.initial_state(wl)
+    st.base.copy_(torch.from_numpy(S0))
+    eg.base.copy_(torch.from_numpy(S0))
+    rng = np.random.default_rng(5)
+    hist = []
+    for tau in range(wl.steps):
+        s, args = _inputs(wl, tau)
+        hist.append(s)
+        st.step_log(*args)
+        eg.step_eager(*args)
+        if (tau + 1) % L == 0:
+            st.merge(B.DL_MERGE_FULL)
+        if tau in (0, 3, L - 1, L + 2, 2 * L + 1, wl.steps - 1):
+            qn = rng.standard_normal((wl.batch, H, d))
+            qs, qf = W.store(qn, wl.dtype)
+            qt = to_torch(qs, wl.dtype)
+            before = (st.base.clone(), st.fill.clone())
+            o_log = st.readout(qt).double().cpu().numpy().reshape(P, d)
+            o_eag = eg.readout(qt).double().cpu().numpy().reshape(P, d)
+            assert torch.equal(before[0], st.base) and torch.equal(before[1], st.fill)
+            T = tau + 1
+            stack = lambda f: np.stack([f(x) for x in hist])
+            _, S_ref = oracle.run(wl.variant, stack(lambda x: x.q_f32.reshape(P, d)),
+                                  stack(lambda x: x.k_f32.reshape(P, d)),
+                                  stack(lambda x: x.v_f32.reshape(P, d)),
+                                  stack(lambda x: x.g.reshape(P, -1) if wl.channel_decay else x.g.reshape(P)),
+                                  None if hist[0].beta is None else stack(lambda x: x.beta.reshape(P)),
+                                  S0.reshape(P, d, d))
+            ref = oracle.readout(S_ref, qf.reshape(P, d))
+            for name, o in (("log", o_log), ("eager", o_eag)):
+                e = per_pair_error(o, ref)
+                assert e.max() <= TOL, (name, tau, e.max())
+    assert st.check() == 0 and eg.check() == 0
+
+
+def test_device_flags():
+    wl = W.GDN_HYBRID.scaled(batch=2, heads=2, steps=4)
+    H, d = wl.heads, wl.d_k
+    st = B.DecodeState(wl.variant, 2, H, d, 2, wl.dtype)
+    _, args = _inputs(wl, 0)
+    st.step_log(*args)
+    st.step_log(*args)
+    assert st.check() == 0 and int(st.fill.max()) == 2
+    base = st.base.clone()
+    o = st.step_log(*args)                       # log is full: rejected
+    assert torch.isnan(o).all()
+    assert st.check() == B.DL_FLAG_LOG_FULL
+    assert st.check() == 0                       # check clears the flags
+    assert torch.equal(base, st.base) and int(st.fill.max()) == 2
+    o = st.step_eager(*args)                     # eager on a non-empty log: rejected
+    assert torch.isnan(o).all() and st.check() == B.DL_FLAG_LOG_NONEMPTY
+    st.merge(B.DL_MERGE_FULL)
+    assert int(st.fill.max()) == 0 and st.check() == 0
+    bad = torch.tensor([0, 7], dtype=torch.int32, device="cuda")
+    o = st.step_log(*args, slot_idx=bad)
+    assert torch.isnan(o[1]).all() and not torch.isnan(o[0]).any()
+    assert st.check() == B.DL_FLAG_BAD_SLOT
+    st.close()
+
+
+def test_permuted_slots_match_identity():
+    """Rows map to units through slot_idx in any order."""
+    wl = W.KDA_SWEEP.scaled(batch=4, heads=2, steps=9)
+    H, d, L = wl.heads, wl.d_k, 4
+    a = B.DecodeState(wl.variant, 4, H, d, L, wl.dtype)
+    b = B.DecodeState(wl.variant, 4, H, d, L, wl.dtype)
+    perm = np.array([2, 0, 3, 1])
+    slot = torch.from_numpy(perm.astype(np.int32)).cuda()
+    for tau in range(wl.steps):
+        _, args = _inputs(wl, tau)
+        oa = a.step_log(*args)
+        pargs = tuple(None if x is None else x[torch.from_numpy(perm).cuda()].contiguous() for x in args)
+        ob = b.step_log(*pargs, slot_idx=slot)
+        assert torch.equal(oa[torch.from_numpy(perm).cuda()], ob)
+        if (tau + 1) % L == 0:
+            a.merge()
+            b.merge(rows=4, slot_idx=slot)
+    assert torch.equal(a.base, b.base) and torch.equal(a.fill, b.fill)
+
+
+def test_zero_rows_and_argument_errors():
+    wl = W.GDN_HYBRID.scaled(batch=2, heads=2, steps=1)
+    H, d = wl.heads, wl.d_k
+    st = B.DecodeState(wl.variant, 2, H, d, 4, wl.dtype)
+    _, (q, k, v, g, beta) = _inputs(wl, 0)
+    o = torch.empty((2, H, d), device="cuda")
+    lib = B.load()
+    h = st.handle
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+    assert lib.dl_decode_step_log(h, 0, None, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(o), None) == 0
+    assert lib.dl_decode_step_log(h, 2, None, ptr(q), ptr(k), ptr(v), ptr(g), None, ptr(o), None) == B.DL_ERR_INVALID
+    assert lib.dl_decode_step_log(h, 3, None, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(o), None) == B.DL_ERR_INVALID
+    mis = ctypes.c_void_p(q.data_ptr() + 2)
+    assert lib.dl_decode_step_eager(h, 2, None, mis, ptr(k), ptr(v), ptr(g), ptr(beta), ptr(o), None) == B.DL_ERR_INVALID
+    assert lib.dl_merge(h, 2, None, 5, None) == B.DL_ERR_INVALID
+    e = B.DecodeState(wl.variant, 2, H, d, 0, wl.dtype)
+    assert lib.dl_decode_step_log(e.handle, 2, None, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(o), None) == B.DL_ERR_INVALID
+    assert st.check() == 0 and int(st.fill.max()) == 0
+    st.close()
+    e.close()
+
+
+@pytest.mark.parametrize("wl,L", [(W.GDN_HYBRID.scaled(batch=3, heads=4, steps=16), 16),
+                                  (W.KDA_SWEEP.scaled(batch=3, heads=4, steps=64), 64),
+                                  (W.RWKV6_ADD.scaled(batch=3, heads=4, steps=32), 32),
+                                  (W.KDA_SWEEP.scaled(batch=2, heads=2, steps=13), 13)],
+                         ids=["gdn16", "kda64", "rwkv32", "kda13-partial"])
+def test_wy_merge_equals_replay_merge(wl, L):
+    """The MFMA WY merge and the step-by-step replay merge agree closely."""
+    H, d = wl.heads, wl.d_k
+    a = B.DecodeState(wl.variant, wl.batch, H, d, L, wl.dtype)
+    b = B.DecodeState(wl.variant, wl.batch, H, d, L, wl.dtype)
+    S0 = torch.from_numpy(W.initial_state(wl.scaled(state_std=0.5)))
+    a.base.copy_(S0)
+    b.base.copy_(S0)
+    for tau in range(wl.steps):
+        _, args = _inputs(wl, tau)
+        a.step_log(*args)
+        b.step_log(*args)
+    a.merge(B.DL_MERGE_ALL)
+    b.merge(B.DL_MERGE_ALL, replay=True)
+    x, y = a.base.double().cpu().numpy(), b.base.double().cpu().numpy()
+    err = per_pair_error(x.reshape(-1, d, d), y.reshape(-1, d, d)).max()
+    log(f"  WY vs replay {wl.name} L={L}: {err:.2e}")
+    assert err <= 1e-5
+    assert int(a.fill.max()) == 0 and int(b.fill.max()) == 0

@@ -1,0 +1,447 @@
+#!/usr/bin/env python3
+"""Decode-time recurrent-state update benchmark on one MI355X: eager vs DeltaLog.
+
+A step is one decode token for every (sequence, layer, head) state of the
+workload: the DeltaLog path appends to the log and reads out from the
+read-only base (dl_decode_step_log), merging full logs into the base in WY
+form (dl_merge); the eager path rewrites every state (dl_decode_step_eager).
+Inputs for all steps are resident in HBM before timing starts.  One JSON
+line is printed:
+
+  value          DeltaLog state updates/s (one update = one state, one token)
+  roofline       the DeltaLog step kernel's algorithmic bytes per launch over
+                 its average HIP-event duration, against 8 TB/s
+  eager          the same for the eager path
+  merge          the merge kernel's bytes and MFMA rate
+  cpu_baseline   the float64 oracle on the host cores, on a bounded sample
+  parity         the sampled GPU outputs and final states against the oracle
+
+Usage: python bench.py [--config 1..5] [--L n] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+from linear_attention_recurrent_gated_amd import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
+METRIC = "recurrent state updates/s + achieved HBM GB/s (% of peak), eager vs DeltaLog"
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte model (bytes the method itself must move per state)
+# ---------------------------------------------------------------------------
+def byte_model(wl: W.Workload):
+    es = 4 if wl.dtype == "f32" else 2
+    dk, dv = wl.d_k, wl.d_v
+    St = 4 * dv * dk                                   # fp32 state
+    g = 4 * dk if wl.channel_decay else 4
+    b = 4 if wl.has_beta else 0
+    In = (2 * dk + dv) * es + g + b                    # q, k, v, g, beta
+    Out = 4 * dv                                       # fp32 o
+    E = (dk + dv) * es + g + b                         # one log entry
+    return dict(St=St, In=In, Out=Out, E=E)
+
+
+def eager_bytes(m):
+    """Per state: read and write S once, read inputs and the fill counter, write o."""
+    return 2 * m["St"] + m["In"] + m["Out"] + 4
+
+
+def log_step_bytes(m, c_prev):
+    """Per state with c_prev logged entries: read S0 and the logged entries,
+    read inputs, append one entry, write o, read and write the fill counter."""
+    return m["St"] + c_prev * m["E"] + m["In"] + m["E"] + m["Out"] + 8
+
+
+def merge_bytes(m, n):
+    """Per merged state: read S0 and n entries, write S0, read and reset fill."""
+    return 2 * m["St"] + n * m["E"] + 8
+
+
+def merge_flops(wl, n):
+    """The two dense contractions per merged state (W = S Kt^T, S += Z Y)."""
+    mult = 1 if wl.variant == W.RWKV6 else 2
+    return 2 * wl.d_v * wl.d_k * n * mult
+
+
+# ---------------------------------------------------------------------------
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "linear_attention_recurrent_gated_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed counter summary, if it matches the sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps before timing")
+    ap.add_argument("--config", type=int, default=2, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--L", type=int, default=None, help="log slots (default: the workload's)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--paths", default="eager,log")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target wall time of the oracle sample")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
+                    help="also run a plain device copy of this size (counter calibration)")
+    return ap.parse_args(argv)
+
+
+class HipEvents:
+    """hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self):
+        import ctypes
+
+        import torch  # noqa: F401  (binds libamdhip64.so.7 to torch's runtime)
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def pair(self):
+        a, b = self.ct.c_void_p(), self.ct.c_void_p()
+        assert self.hip.hipEventCreate(self.ct.byref(a)) == 0
+        assert self.hip.hipEventCreate(self.ct.byref(b)) == 0
+        self.made += [a, b]
+        return a, b
+
+    def ms(self, a, b) -> float:
+        f = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(f), a, b)
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return float(f.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(e)
+        self.made = []
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every state is independent, so more GPUs would each run their own share)",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import oracle
+    from linear_attention_recurrent_gated_amd import binding as B
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    B.load()
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.config]
+    L = args.L or (16 if args.config == 3 else wl.log_lens[0])
+    K = args.steps or wl.steps
+    Wu = args.warmup if args.warmup is not None else 2 * L
+    prefix = wl.prefix_steps(L)
+    T = prefix + Wu + K
+    H, d, Bt, layers = wl.heads, wl.d_k, wl.batch, wl.layers
+    U = wl.units_total
+    P = U * H
+    paths = args.paths.split(",")
+    m = byte_model(wl)
+    log(f"[bench] {wl.name}: variant {W.VARIANT_NAMES[wl.variant]}, {P} states, d={d}, L={L}, "
+        f"steps {prefix}+{Wu}+{K}, inputs {wl.dtype}")
+
+    # ---- inputs for every step, resident on the device
+    t0 = time.time()
+    first = W.first_active_step(wl, L, args.seed)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    Q = torch.empty((T, U, H, d), dtype=tdt, device=dev)
+    Kt = torch.empty_like(Q)
+    V = torch.empty_like(Q)
+    G = torch.empty((T, U, H, d) if wl.channel_decay else (T, U, H), dtype=torch.float32, device=dev)
+    Bb = torch.empty((T, U, H), dtype=torch.float32, device=dev) if wl.has_beta else None
+    # oracle sample: calibrate its speed, then pick how many states it takes
+    sample_cap = P
+    if not args.no_cpu_baseline:
+        rng = np.random.default_rng(1)
+        n_cal = 4
+        qc = rng.standard_normal((16, n_cal, d)).astype(np.float32)
+        gc = -np.abs(rng.standard_normal((16, n_cal, d) if wl.channel_decay else (16, n_cal))).astype(np.float32)
+        bc = rng.random((16, n_cal)).astype(np.float32)
+        tc = time.time()
+        oracle.run(wl.variant, qc, qc, qc, gc, bc, threads=1)
+        per_core = 16 * n_cal / max(time.time() - tc, 1e-6)
+        threads = min(16, oracle.default_threads())
+        sample_cap = int(max(1, min(P, args.cpu_seconds * per_core * threads / T)))
+    sample = np.unique(np.linspace(0, P - 1, num=sample_cap).round().astype(np.int64))
+    sq, sk, sv, sg, sb = [], [], [], [], []
+    blocks = [list(range(i, min(T, i + 32))) for i in range(0, T, 32)]
+    for block in blocks:
+        for tau, s in zip(block, W.draw_steps(wl, block, args.seed)):
+            if wl.dtype == "bf16":
+                cv = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+            else:
+                cv = torch.from_numpy
+            Q[tau].copy_(cv(s.q))
+            Kt[tau].copy_(cv(s.k))
+            V[tau].copy_(cv(s.v))
+            G[tau].copy_(torch.from_numpy(s.g))
+            if Bb is not None:
+                Bb[tau].copy_(torch.from_numpy(s.beta))
+            if not args.no_cpu_baseline:
+                sq.append(s.q_f32.reshape(P, d)[sample])
+                sk.append(s.k_f32.reshape(P, d)[sample])
+                sv.append(s.v_f32.reshape(P, d)[sample])
+                sg.append(s.g.reshape(P, -1)[sample] if wl.channel_decay else s.g.reshape(P)[sample])
+                if s.beta is not None:
+                    sb.append(s.beta.reshape(P)[sample])
+    S0 = W.initial_state(wl, args.seed)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s "
+        f"({(Q.numel() * 3 * Q.element_size() + G.numel() * 4) / 2**30:.2f} GiB on device)")
+
+    # per-step row sets (ragged prefix only)
+    act = [np.nonzero(first <= tau)[0] for tau in range(T)]
+    gathers = {}
+    for tau in range(prefix):
+        a = act[tau]
+        if 0 < len(a) < Bt:
+            gathers[tau] = (torch.from_numpy(a.astype(np.int64)).to(dev),
+                            torch.from_numpy(a.astype(np.int32)).to(dev), len(a))
+
+    results = {}
+    for path in paths:
+        states = []
+        for l in range(layers):
+            st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype, device=dev)
+            st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
+            states.append(st)
+        O = torch.zeros((T, U, H, d), dtype=torch.float32, device=dev)
+        stream = torch.cuda.current_stream().cuda_stream
+        lib = B.load()
+        step_fn = lib.dl_decode_step_eager if path == "eager" else lib.dl_decode_step_log
+        fills = np.zeros(Bt, dtype=np.int64)     # host model of each sequence's log fill
+        keep = []                                # gathered inputs of ragged prefix steps
+
+        # every launch of the run, with its arguments, decided before anything runs
+        plan = []                                # (tau, kind, handle, args)
+        for tau in range(T):
+            for l in range(layers):
+                st = states[l]
+                lo, hi = l * Bt, (l + 1) * Bt
+                if len(act[tau]) == 0:
+                    continue
+                if tau in gathers:
+                    idx, slot, rows = gathers[tau]
+                    xs = [x[tau, lo:hi].index_select(0, idx).contiguous() for x in (Q, Kt, V, G)]
+                    xs.append(Bb[tau, lo:hi].index_select(0, idx).contiguous() if Bb is not None else None)
+                    o = torch.empty((rows, H, d), dtype=torch.float32, device=dev)
+                    keep.append((xs, o, l, tau))
+                    sp = slot.data_ptr()
+                else:
+                    xs = [Q[tau, lo:hi], Kt[tau, lo:hi], V[tau, lo:hi], G[tau, lo:hi],
+                          None if Bb is None else Bb[tau, lo:hi]]
+                    rows, sp, o = Bt, None, O[tau, lo:hi]
+                ptrs = [None if x is None else x.data_ptr() for x in xs]
+                plan.append((tau, "step", st.handle, (rows, sp, *ptrs, o.data_ptr(), stream)))
+                if path != "eager":
+                    if l == 0:
+                        fills[act[tau]] += 1
+                    if wl.ragged or np.any(fills == L):
+                        plan.append((tau, "merge", st.handle, (Bt, None, B.DL_MERGE_FULL, stream)))
+                    if l == layers - 1:
+                        fills[fills == L] = 0
+        t_first = prefix + Wu
+        timed = [(kind, h, a) for tau, kind, h, a in plan if tau >= t_first]
+        ev = HipEvents()
+        evs = [ev.pair() for _ in timed]
+
+        def run(entries, events=None):
+            for i, (kind, h, a) in enumerate(entries):
+                if events is not None:
+                    lib.dl_time_next_launch(h, events[i][0], events[i][1])
+                rc = step_fn(h, *a) if kind == "step" else lib.dl_merge(h, *a)
+                if rc != 0:
+                    raise RuntimeError(f"{kind} failed: {B.dl_last_error()}")
+
+        run([(kind, h, a) for tau, kind, h, a in plan if tau < t_first])
+        for xs, o, l, tau in keep:
+            O[tau, l * Bt:(l + 1) * Bt].index_copy_(0, gathers[tau][0], o)
+        fills_at_start = np.zeros(Bt, dtype=np.int64)
+        for tau in range(t_first):
+            fills_at_start[act[tau]] += 1
+            fills_at_start[fills_at_start == L] = 0
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        run(timed, evs)
+        ev1.record()
+        torch.cuda.synchronize()
+        total_ms = ev0.elapsed_time(ev1)
+        step_ms = [ev.ms(*e) for (kind, _, _), e in zip(timed, evs) if kind == "step"]
+        merge_ms = [ev.ms(*e) for (kind, _, _), e in zip(timed, evs) if kind == "merge"]
+        ev.close()
+        if path != "eager":
+            for st in states:
+                B.dl_merge(st.handle, Bt, None, B.DL_MERGE_ALL, stream)
+        flags = [st.check() for st in states]
+        assert not any(flags), f"device flags {flags}"
+        # algorithmic bytes of the timed launches
+        if path == "eager":
+            step_bytes = [eager_bytes(m) * Bt * H] * len(step_ms)
+            mbytes, mflops = 0, 0
+        else:
+            step_bytes, mbytes, mflops = [], 0.0, 0.0
+            f = fills_at_start.copy()
+            for tau in range(prefix + Wu, T):
+                for l in range(layers):
+                    step_bytes.append(float(np.sum([log_step_bytes(m, c) for c in f])) * H)
+                    if l == layers - 1:
+                        f += 1
+                        full = f == L
+                        if wl.ragged or full.any():     # a merge launch ran after this step
+                            mbytes += layers * H * (merge_bytes(m, L) * full.sum() + 4 * (~full).sum())
+                            mflops += layers * H * merge_flops(wl, L) * full.sum()
+                        f[full] = 0
+        kern_s = sum(step_ms) / 1e3
+        res = dict(
+            total_ms=total_ms,
+            ms_per_step=total_ms / K,
+            updates_per_s=P * K / (total_ms / 1e3),
+            step_kernel_avg_us=1e3 * float(np.mean(step_ms)),
+            step_kernel_launches=len(step_ms),
+            step_kernel_GBps=sum(step_bytes) / kern_s / 1e9,
+            step_bytes_per_launch=float(np.mean(step_bytes)),
+            merge_launches=len(merge_ms),
+            merge_ms_total=float(np.sum(merge_ms)) if merge_ms else 0.0,
+            merge_bytes=mbytes,
+            merge_flops=mflops,
+        )
+        # sampled outputs and final states for the parity check
+        su, sh = torch.from_numpy(sample // H).to(dev), torch.from_numpy(sample % H).to(dev)
+        res["o_sample"] = O[:, su, sh].double().cpu().numpy()            # [T, n, d]
+        Sfull = torch.cat([st.base for st in states], 0)
+        res["S_sample"] = Sfull[su, sh].double().cpu().numpy()
+        results[path] = res
+        for st in states:
+            st.close()
+        del O, Sfull
+        log(f"[bench] {path}: {res['ms_per_step'] * 1e3:.1f} us/step, "
+            f"{res['updates_per_s']:.3e} upd/s, step kernel {res['step_kernel_avg_us']:.1f} us "
+            f"({res['step_kernel_GBps']:.0f} GB/s), merges {len(merge_ms)} "
+            f"({res['merge_ms_total']:.3f} ms)")
+
+    if args.copy_probe:
+        n = args.copy_probe * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copy probe: {args.copy_probe} MiB copied 3 times")
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": K, "warmup": Wu, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "unit": "state updates/s"}
+    out["config"] = {"workload": wl.name, "variant": W.VARIANT_NAMES[wl.variant],
+                     "batch": Bt, "layers": layers, "heads": H, "d_k": d, "d_v": wl.d_v,
+                     "log_len": L, "input_dtype": wl.dtype, "state_dtype": "fp32",
+                     "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix}
+    main_path = "log" if "log" in results else paths[0]
+    r = results[main_path]
+    out["value"] = r["updates_per_s"]
+    out["ms_per_step"] = r["ms_per_step"]
+    kname = "log_step_kernel" if main_path == "log" else "eager_step_kernel"
+    out["roofline"] = {"bound": "hbm", "kernel": kname,
+                       "achieved": r["step_kernel_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                       "frac": r["step_kernel_GBps"] / HBM_PEAK_GBPS,
+                       "avg_launch_us": r["step_kernel_avg_us"],
+                       "algorithmic_bytes_per_launch": r["step_bytes_per_launch"],
+                       "traffic": counter_traffic(kname, wl.name)}
+    if "eager" in results and main_path != "eager":
+        e = results["eager"]
+        out["eager"] = {"value": e["updates_per_s"], "ms_per_step": e["ms_per_step"],
+                        "kernel": "eager_step_kernel", "achieved_GBps": e["step_kernel_GBps"],
+                        "frac": e["step_kernel_GBps"] / HBM_PEAK_GBPS,
+                        "avg_launch_us": e["step_kernel_avg_us"],
+                        "algorithmic_bytes_per_launch": e["step_bytes_per_launch"],
+                        "traffic": counter_traffic("eager_step_kernel", wl.name)}
+        out["speedup_vs_eager"] = r["updates_per_s"] / e["updates_per_s"]
+    if main_path == "log" and r["merge_launches"]:
+        ms = r["merge_ms_total"] / 1e3
+        out["merge"] = {"kernel": "merge_wy_kernel", "launches": r["merge_launches"],
+                        "share_of_step_time": r["merge_ms_total"] / r["total_ms"],
+                        "GBps": r["merge_bytes"] / ms / 1e9 if ms else None,
+                        "mfma_TFLOPs": r["merge_flops"] / ms / 1e12 if ms else None,
+                        "mfma_frac": (r["merge_flops"] / ms / 1e12 / FP32_MFMA_PEAK_TFLOPS) if ms else None}
+
+    # ---- the oracle on the host cores, same inputs, sampled states
+    if not args.no_cpu_baseline:
+        threads = min(16, oracle.default_threads())
+        t_start = np.tile(first, layers)[sample // H]
+        tc = time.time()
+        o_ref, S_ref = oracle.run(wl.variant, np.stack(sq), np.stack(sk), np.stack(sv),
+                                  np.stack(sg), np.stack(sb) if sb else None,
+                                  S0.reshape(P, d, d)[sample], t_start, threads=threads)
+        dt = time.time() - tc
+        n_upd = int(np.sum(T - t_start))
+        out["cpu_baseline"] = {"value": n_upd / dt, "unit": "state updates/s", "cores": threads,
+                               "kind": "oracle", "seconds": dt,
+                               "sample": f"{len(sample)} of {P} states (evenly spaced), all {T} steps "
+                                         f"({n_upd} updates), float64"}
+        parity = {}
+        for path, res in results.items():
+            o = res["o_sample"]
+            scale_o = np.maximum(1.0, np.abs(o_ref).max(axis=(0, 2)))
+            eo = (np.abs(o - o_ref).max(axis=(0, 2)) / scale_o).max()
+            scale_s = np.maximum(1.0, np.abs(S_ref).reshape(len(sample), -1).max(axis=1))
+            es = (np.abs(res["S_sample"] - S_ref).reshape(len(sample), -1).max(axis=1) / scale_s).max()
+            parity[path] = {"max_rel_err_outputs": float(eo), "max_rel_err_state": float(es),
+                            "ok": bool(eo <= 2e-4 and es <= 2e-4)}
+        out["parity"] = parity
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

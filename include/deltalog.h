@@ -178,6 +178,15 @@ dl_status dl_readout(dl_state *st, int32_t rows, const int32_t *slot_idx, const 
  * NULL), clear it, and return DL_ERR_STATE if any bit was set. */
 dl_status dl_state_check(dl_state *st, void *stream, int32_t *flags_out);
 
+/* Profiling hook: the next kernel this handle launches records `start_event`
+ * and `stop_event` (hipEvent_t values the caller created, with timing) at
+ * its own dispatch begin and end, so hipEventElapsedTime between them is
+ * that kernel's execution time alone, without launch gaps.  One-shot: the
+ * next launching call consumes them (calls that launch nothing leave them
+ * armed); NULL, NULL disarms.  The events must belong to the same device
+ * and HIP runtime as the stream. */
+dl_status dl_time_next_launch(dl_state *st, void *start_event, void *stop_event);
+
 /* Message for the latest non-OK status on this thread ("" if none). */
 const char *dl_last_error(void);
 

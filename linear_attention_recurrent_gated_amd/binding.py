@@ -57,6 +57,7 @@ _SIGS = {
     "dl_merge_replay": (_I, [_P, _I, _P, _I, _P]),
     "dl_readout": (_I, [_P, _I, _P, _P, _P, _P]),
     "dl_state_check": (_I, [_P, _P, ctypes.POINTER(_I)]),
+    "dl_time_next_launch": (_I, [_P, _P, _P]),
     "dl_last_error": (ctypes.c_char_p, []),
     "dl_version": (_I, []),
 }
@@ -68,6 +69,10 @@ def load(path: str = LIB_PATH):
     """Load the library (once) and declare every entry point's signature."""
     global _lib
     if _lib is None:
+        # torch bundles its own HIP runtime under the same soname; loading it
+        # first makes this library bind to that one runtime, so streams,
+        # events and allocations are shared.
+        import torch  # noqa: F401
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
         lib = ctypes.CDLL(path)
@@ -137,6 +142,10 @@ def dl_merge_replay(handle, rows, slot_idx, mode, stream) -> None:
 
 def dl_readout(handle, rows, slot_idx, q, o, stream) -> None:
     _check(load().dl_readout(handle, rows, slot_idx, q, o, stream))
+
+
+def dl_time_next_launch(handle, start_event, stop_event) -> None:
+    _check(load().dl_time_next_launch(handle, start_event, stop_event))
 
 
 def dl_state_check(handle, stream) -> int:

@@ -15,6 +15,7 @@ struct dl_state {
     dl::Params p;
     void *mem;
     size_t bytes;
+    hipEvent_t ev_start, ev_stop;   // armed by dl_time_next_launch, consumed by one launch
 };
 
 namespace {
@@ -145,7 +146,14 @@ dl_status check_lds(const dl_state *st) {
     return DL_OK;
 }
 
-dl_status launched(hipError_t e, const char *what) {
+dl::Launch launch_of(const dl_state *st, void *stream) {
+    return dl::Launch{static_cast<hipStream_t>(stream), st->ev_start, st->ev_stop};
+}
+
+// Result of one launch; a launch consumes the events dl_time_next_launch armed.
+dl_status launched(dl_state *st, hipError_t e, const char *what) {
+    st->ev_start = nullptr;
+    st->ev_stop = nullptr;
     if (e != hipSuccess)
         return fail(DL_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
     return ok();
@@ -180,6 +188,8 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     if (!st)
         return fail(DL_ERR_INVALID, "out of host memory");
     st->desc = *desc;
+    st->ev_start = nullptr;
+    st->ev_stop = nullptr;
     st->mem = dev_mem;
     st->bytes = bytes;
     char *m = static_cast<char *>(dev_mem);
@@ -199,7 +209,8 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.log_g = has_log ? reinterpret_cast<float *>(m + l.off_g) : nullptr;
     p.log_beta = (has_log && desc->variant != DL_RWKV6) ? reinterpret_cast<float *>(m + l.off_b)
                                                         : nullptr;
-    const hipError_t e = dl::launch_zero(dev_mem, l.total, static_cast<hipStream_t>(stream));
+    const hipError_t e = dl::launch_zero(dev_mem, l.total,
+                                         dl::Launch{static_cast<hipStream_t>(stream), nullptr, nullptr});
     if (e != hipSuccess) {
         delete st;
         return fail(DL_ERR_LAUNCH, "zeroing the state block: %s", hipGetErrorString(e));
@@ -234,8 +245,8 @@ dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_i
         return s;
     if (rows == 0)
         return ok();
-    return launched(dl::launch_eager(st->p, rows, slot_idx, q, k, v, g, beta, o,
-                                     static_cast<hipStream_t>(stream)),
+    return launched(st, dl::launch_eager(st->p, rows, slot_idx, q, k, v, g, beta, o,
+                                         launch_of(st, stream)),
                     "eager step launch");
 }
 
@@ -252,8 +263,8 @@ dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx
         return s;
     if (rows == 0)
         return ok();
-    return launched(dl::launch_log_step(st->p, rows, slot_idx, q, k, v, g, beta, o,
-                                        static_cast<hipStream_t>(stream)),
+    return launched(st, dl::launch_log_step(st->p, rows, slot_idx, q, k, v, g, beta, o,
+                                            launch_of(st, stream)),
                     "log step launch");
 }
 
@@ -266,10 +277,10 @@ static dl_status merge_common(dl_state *st, int32_t rows, const int32_t *slot_id
         return fail(DL_ERR_INVALID, "unknown merge mode %d", mode);
     if (st->desc.log_len < 1 || rows == 0)
         return ok();
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const hipError_t e = wy ? dl::launch_merge_wy(st->p, rows, slot_idx, mode, hs)
-                            : dl::launch_merge_replay(st->p, rows, slot_idx, mode, hs);
-    return launched(e, "merge launch");
+    const dl::Launch ln = launch_of(st, stream);
+    const hipError_t e = wy ? dl::launch_merge_wy(st->p, rows, slot_idx, mode, ln)
+                            : dl::launch_merge_replay(st->p, rows, slot_idx, mode, ln);
+    return launched(st, e, "merge launch");
 }
 
 dl_status dl_merge(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
@@ -296,7 +307,7 @@ dl_status dl_readout(dl_state *st, int32_t rows, const int32_t *slot_idx, const 
         return s;
     if (rows == 0)
         return ok();
-    return launched(dl::launch_readout(st->p, rows, slot_idx, q, o, static_cast<hipStream_t>(stream)),
+    return launched(st, dl::launch_readout(st->p, rows, slot_idx, q, o, launch_of(st, stream)),
                     "readout launch");
 }
 
@@ -313,11 +324,21 @@ dl_status dl_state_check(dl_state *st, void *stream, int32_t *flags_out) {
     if (flags_out)
         *flags_out = h;
     if (h != 0) {
-        e = dl::launch_zero(st->p.flags, 256, hs);
+        e = dl::launch_zero(st->p.flags, 256, dl::Launch{hs, nullptr, nullptr});
         if (e != hipSuccess)
             return fail(DL_ERR_LAUNCH, "clearing device flags: %s", hipGetErrorString(e));
         return fail(DL_ERR_STATE, "device flags 0x%x (1: log full, 2: eager on non-empty log, 4: bad slot)", h);
     }
+    return ok();
+}
+
+dl_status dl_time_next_launch(dl_state *st, void *start_event, void *stop_event) {
+    if (!st)
+        return fail(DL_ERR_INVALID, "state handle is NULL");
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(DL_ERR_INVALID, "give both events or neither");
+    st->ev_start = static_cast<hipEvent_t>(start_event);
+    st->ev_stop = static_cast<hipEvent_t>(stop_event);
     return ok();
 }
 

@@ -11,6 +11,7 @@
 // sum in all 8 lanes.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -178,20 +179,27 @@ __device__ __forceinline__ float4 lds_load4(const unsigned char *base, int elem)
 }
 
 // ---------------------------------------------------------------------------
-// host launchers (defined in dl_step.hip / dl_merge.hip)
+// host launchers (defined in dl_step.hip / dl_merge.hip).  Every kernel goes
+// through hipExtLaunchKernelGGL so that optional start/stop events are
+// recorded by the dispatch itself.
 // ---------------------------------------------------------------------------
-hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t start, stop;
+};
+
+hipError_t launch_zero(void *p, size_t bytes, const Launch &ln);
 hipError_t launch_eager(const Params &P, int rows, const int *slot_idx, const void *q,
                         const void *k, const void *v, const float *g, const float *beta,
-                        float *o, hipStream_t stream);
+                        float *o, const Launch &ln);
 hipError_t launch_log_step(const Params &P, int rows, const int *slot_idx, const void *q,
                            const void *k, const void *v, const float *g, const float *beta,
-                           float *o, hipStream_t stream);
+                           float *o, const Launch &ln);
 hipError_t launch_readout(const Params &P, int rows, const int *slot_idx, const void *q,
-                          float *o, hipStream_t stream);
+                          float *o, const Launch &ln);
 hipError_t launch_merge_replay(const Params &P, int rows, const int *slot_idx, int mode,
-                               hipStream_t stream);
+                               const Launch &ln);
 hipError_t launch_merge_wy(const Params &P, int rows, const int *slot_idx, int mode,
-                           hipStream_t stream);
+                           const Launch &ln);
 
 }  // namespace dl

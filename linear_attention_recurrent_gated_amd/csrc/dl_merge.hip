@@ -147,7 +147,12 @@ __global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *
 }
 
 // ---------------------------------------------------------------------------
-// WY merge (MFMA)
+// WY merge (MFMA).  Four waves per (unit, head); each holds D/4 value rows of
+// the base in MFMA layout for the whole merge.  Per chunk, the key side
+// (decayed keys, pairwise-decay Gram, Y by back substitution) is built in
+// LDS by all threads in three short phases, then each wave runs the two
+// contractions on its rows.  The value loads of the chunk are issued before
+// the key-side phases so they overlap them.
 // ---------------------------------------------------------------------------
 template <int V, int D, typename T>
 __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__restrict__ slot_idx,
@@ -158,8 +163,8 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
     constexpr int KS = D + 4;           // padded LDS row stride (floats)
     __shared__ __align__(16) float sKt[C * KS];   // k_j exp(Lam_j)
     __shared__ __align__(16) float sY[C * KS];    // rows of diag(beta)(I+M)^{-1} Kh
-    __shared__ float sLam[C * D];                 // chunk-local cumulative log-decay
-    __shared__ float sK[C * D];                   // keys, fp32
+    __shared__ __align__(16) float sK[C * KS];    // keys, fp32
+    __shared__ __align__(16) float sLam[C * KS];  // chunk-local cumulative log-decay
     __shared__ float sM[C * C];                   // beta_j G_ij, i < j
     __shared__ float sB[C];
     __shared__ __align__(16) float sELC[D];       // exp(Lam_C) per key channel
@@ -177,7 +182,7 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
     const float *Gl = P.log_g + pair * L * ((V == GDN) ? 1 : D);
     const float *Bl = P.log_beta + pair * L;
 
-    // base rows in MFMA operand layout: st[it][m].e = S[16 (wave NIT + it) + li][4 kg + 16 m + e]
+    // base rows in MFMA operand layout: st[it][m][e] = S[16 (wave NIT + it) + li][4 kg + 16 m + e]
     floatx4 st[NIT][NM];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -191,38 +196,62 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
 
     for (int j0 = 0; j0 < n; j0 += C) {
         const int cnt = (n - j0) < C ? (n - j0) : C;
-        __syncthreads();   // previous chunk's LDS reads are done
+        // this chunk's logged values for the Z tiles (clamped, branch-free loads)
+        floatx4 vv[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int row = 16 * (wave * NIT + it) + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 4 * kg + r;
+                const float x = Elem<T>::load1(Vl + (size_t)(j0 + (j < cnt ? j : cnt - 1)) * D + row);
+                vv[it][r] = (j < cnt) ? x : 0.f;
+            }
+        }
+        __syncthreads();   // the previous chunk's LDS operands are consumed
 
-        // ---- stage: thread c walks its key channel through the chunk
-        float lam_r[C], kr[C];
+        // ---- phase 1a: raw keys and log-decays of the chunk into LDS (zeros past cnt)
+        for (int idx = tid; idx < C * (D / 4); idx += 256) {
+            const int j = idx / (D / 4), c = 4 * (idx - j * (D / 4));
+            const int e = j0 + (j < cnt ? j : cnt - 1);
+            float4 kv = Elem<T>::load4(Kl + (size_t)e * D + c);
+            float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (V != GDN)
+                gv = *reinterpret_cast<const float4 *>(Gl + (size_t)e * D + c);
+            if (j >= cnt) {
+                kv = make_float4(0.f, 0.f, 0.f, 0.f);
+                gv = kv;
+            }
+            *reinterpret_cast<float4 *>(&sK[j * KS + c]) = kv;
+            if constexpr (V != GDN)
+                *reinterpret_cast<float4 *>(&sLam[j * KS + c]) = gv;
+        }
+        if (tid < C) {
+            const int e = j0 + (tid < cnt ? tid : cnt - 1);
+            sB[tid] = (V != RWKV6 && tid < cnt) ? Bl[e] : 0.f;
+            if constexpr (V == GDN)
+                sM[tid] = (tid < cnt) ? Gl[e] : 0.f;      // scratch: scalar log-decays
+        }
+        __syncthreads();
+        // ---- phase 1b: thread c accumulates the decay of key channel c through the chunk
         if (tid < D) {
             const int c = tid;
             float lam = 0.f;
-#pragma unroll
             for (int j = 0; j < C; ++j) {
-                float kk = 0.f;
-                if (j < cnt) {
-                    const int e = j0 + j;
-                    lam += (V == GDN) ? Gl[e] : Gl[(size_t)e * D + c];
-                    kk = Elem<T>::load1(Kl + (size_t)e * D + c);
-                }
-                lam_r[j] = lam;
-                kr[j] = kk;
-                sKt[j * KS + c] = kk * expf(lam);
-                sLam[j * D + c] = lam;
-                sK[j * D + c] = kk;
+                lam += (V == GDN) ? sM[j] : sLam[j * KS + c];
+                const float kr = sK[j * KS + c];
+                sKt[j * KS + c] = kr * expf(lam);
+                sLam[j * KS + c] = lam;
             }
             sELC[c] = expf(lam);
         }
-        if (tid < C)
-            sB[tid] = (V != RWKV6 && tid < cnt) ? Bl[j0 + tid] : 0.f;
         __syncthreads();
 
-        // ---- Gram with pairwise decay: two lanes per pair (i < j), halves of the channels
+        // ---- phase 2: Gram with pairwise decay, two lanes per pair (i < j), halves of the channels
         if constexpr (V != RWKV6) {
             const int p = tid >> 1, half = tid & 1;
             int i = 0, j = 1;
-            bool inpair = p < C * (C - 1) / 2;
+            const bool inpair = p < C * (C - 1) / 2;
             if (inpair) {
                 int base = 0;
                 while (base + j <= p) {
@@ -235,27 +264,37 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
             float gsum = 0.f;
             if (valid) {
                 const int c0 = half * (D / 2);
-                for (int c = c0; c < c0 + D / 2; ++c) {
-                    const float kk = sK[i * D + c] * sK[j * D + c];
-                    gsum += (V == GDN) ? kk : kk * expf(sLam[j * D + c] - sLam[i * D + c]);
+#pragma unroll 2
+                for (int c = c0; c < c0 + D / 2; c += 4) {
+                    const float4 a = *reinterpret_cast<const float4 *>(&sK[i * KS + c]);
+                    const float4 b = *reinterpret_cast<const float4 *>(&sK[j * KS + c]);
+                    if constexpr (V == GDN) {
+                        gsum += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+                    } else {
+                        const float4 l1 = *reinterpret_cast<const float4 *>(&sLam[i * KS + c]);
+                        const float4 l2 = *reinterpret_cast<const float4 *>(&sLam[j * KS + c]);
+                        gsum += a.x * b.x * expf(l2.x - l1.x) + a.y * b.y * expf(l2.y - l1.y) +
+                                a.z * b.z * expf(l2.z - l1.z) + a.w * b.w * expf(l2.w - l1.w);
+                    }
                 }
             }
             gsum += dpp_mov<0xB1>(gsum);   // add the other half (adjacent lane)
             if (V == GDN && valid)
-                gsum *= expf(sLam[j * D] - sLam[i * D]);
+                gsum *= expf(sLam[j * KS] - sLam[i * KS]);
             if (inpair && half == 0)
                 sM[i * C + j] = valid ? sB[j] * gsum : 0.f;
         }
         __syncthreads();
 
-        // ---- Y = diag(beta) (I + M)^{-1} Kh by back substitution, one channel per thread
+        // ---- phase 3: Y = diag(beta) (I + M)^{-1} Kh, Kh_j = k_j exp(Lam_C - Lam_j)
         if (tid < D) {
             const int c = tid;
-            const float lamC = lam_r[C - 1];
+            const float lamC = sLam[(C - 1) * KS + c];
             float x[C];
 #pragma unroll
             for (int j = C - 1; j >= 0; --j) {
-                float kh = (j < cnt) ? kr[j] * expf(lamC - lam_r[j]) : 0.f;
+                __builtin_amdgcn_sched_barrier(0);   // keep this row's LDS reads from being hoisted
+                float kh = sK[j * KS + c] * expf(lamC - sLam[j * KS + c]);
                 if constexpr (V != RWKV6) {
 #pragma unroll
                     for (int m = j + 1; m < C; ++m)
@@ -269,8 +308,7 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
         }
         __syncthreads();
 
-        // ---- W^T = Kt S^T (MFMA), Z^T = V^T - W^T in the output layout:
-        //      z[it][r] = Z[row 16 (wave NIT + it) + li][entry 4 kg + r]
+        // ---- W^T = Kt S^T (MFMA); Z^T = V^T - W^T: z[it][r] = Z[row 16 (wave NIT + it) + li][entry 4 kg + r]
         floatx4 z[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
@@ -278,6 +316,8 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
             if constexpr (V != RWKV6) {
 #pragma unroll
                 for (int m = 0; m < NM; ++m) {
+                    if (m % 2 == 0)
+                        __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
                     const float4 a = *reinterpret_cast<const float4 *>(&sKt[li * KS + 4 * kg + 16 * m]);
                     acc = mfma16x16x4(a.x, st[it][m][0], acc);
                     acc = mfma16x16x4(a.y, st[it][m][1], acc);
@@ -285,18 +325,13 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
                     acc = mfma16x16x4(a.w, st[it][m][3], acc);
                 }
             }
-            const int row = 16 * (wave * NIT + it) + li;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 4 * kg + r;
-                const float vv = (j < cnt) ? Elem<T>::load1(Vl + (size_t)(j0 + j) * D + row) : 0.f;
-                z[it][r] = vv - acc[r];
-            }
+            z[it] = vv[it] - acc;
         }
-
         // ---- S'^T = diag(exp Lam_C) S^T + Y^T Z^T (MFMA, accumulating in place)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
+            if (m % 2 == 0)
+                __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
             const float4 el = *reinterpret_cast<const float4 *>(&sELC[4 * kg + 16 * m]);
             float a[4];
 #pragma unroll
@@ -355,30 +390,30 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
 
 template <int V, int D, typename T>
 static hipError_t replay_t(const Params &P, int rows, const int *slot_idx, int mode,
-                           hipStream_t stream) {
+                           const Launch &ln) {
     const int CH = P.L < 32 ? P.L : 32;
     const LdsPlan lp = lds_plan(V, D, (int)sizeof(T), CH, P.L, true);
-    hipLaunchKernelGGL((merge_replay_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), lp.bytes,
-                       stream, P, slot_idx, mode);
+    hipExtLaunchKernelGGL((merge_replay_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), lp.bytes,
+                       ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode);
     return hipGetLastError();
 }
 
 template <int V, int D, typename T>
 static hipError_t wy_t(const Params &P, int rows, const int *slot_idx, int mode,
-                       hipStream_t stream) {
-    hipLaunchKernelGGL((merge_wy_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), 0, stream, P,
+                       const Launch &ln) {
+    hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start, ln.stop, 0, P,
                        slot_idx, mode);
     return hipGetLastError();
 }
 
 hipError_t launch_merge_replay(const Params &P, int rows, const int *slot_idx, int mode,
-                               hipStream_t stream) {
-    DL_DISPATCH_M(P, replay_t, P, rows, slot_idx, mode, stream);
+                               const Launch &ln) {
+    DL_DISPATCH_M(P, replay_t, P, rows, slot_idx, mode, ln);
 }
 
 hipError_t launch_merge_wy(const Params &P, int rows, const int *slot_idx, int mode,
-                           hipStream_t stream) {
-    DL_DISPATCH_M(P, wy_t, P, rows, slot_idx, mode, stream);
+                           const Launch &ln) {
+    DL_DISPATCH_M(P, wy_t, P, rows, slot_idx, mode, ln);
 }
 
 }  // namespace dl

@@ -93,8 +93,15 @@ typedef struct {
  *   base     [units, H, d_v, d_k] fp32  -- the dense state (eager) or base (DeltaLog)
  *   log_k    [units, H, L, d_k] in_dtype -- logged keys, bit copies of the inputs
  *   log_v    [units, H, L, d_v] in_dtype -- logged values
- *   log_g    [units, H, L] (GDN) or [units, H, L, d_k] (KDA, RWKV6) fp32 log-decays
+ *   log_g    [units, H, L] (GDN) or [units, H, L, d_k] (KDA, RWKV6) fp32 -- the
+ *            log-decay accumulated from the log's first entry through each
+ *            entry (Lam_j = Lam_{j-1} + g_j in fp32, Lam_{-1} = 0)
  *   log_beta [units, H, L] fp32 (NULL for RWKV6)
+ *   log_t    [units, H, L(L-1)/2] fp32 -- key-side factors of the log (delta-
+ *            rule variants): the inverse R of the unit upper-triangular
+ *            coupling matrix of the logged entries, column j (rows 0..j-1)
+ *            at offset j(j-1)/2, written when entry j is appended and read
+ *            by every readout (NULL for RWKV6 and when L < 2)
  *   fill     [units, H] int32 -- entries in each log; every head of a unit
  *            advances together, one writer per counter
  *   flags    [1] int32 -- DL_FLAG_* bits
@@ -105,6 +112,7 @@ typedef struct {
     void *log_v;
     float *log_g;
     float *log_beta;
+    float *log_t;
     int32_t *fill;
     int32_t *flags;
 } dl_state_ptrs;

@@ -34,7 +34,7 @@ class DlDesc(ctypes.Structure):
 class DlStatePtrs(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("log_k", ctypes.c_void_p),
                 ("log_v", ctypes.c_void_p), ("log_g", ctypes.c_void_p),
-                ("log_beta", ctypes.c_void_p), ("fill", ctypes.c_void_p),
+                ("log_beta", ctypes.c_void_p), ("log_t", ctypes.c_void_p), ("fill", ctypes.c_void_p),
                 ("flags", ctypes.c_void_p)]
 
 
@@ -166,7 +166,8 @@ class DecodeState:
     ``base`` ``[units, H, d, d]`` fp32, ``fill`` ``[units, H]`` int32, and the
     log views ``log_k``/``log_v`` ``[units, H, L, d]`` (input dtype),
     ``log_g`` ``[units, H, L]`` or ``[units, H, L, d]``, ``log_beta``
-    ``[units, H, L]``.
+    ``[units, H, L]`` and ``log_t`` ``[units, H, L(L-1)/2]`` (the packed
+    key-side factors of the delta-rule variants).
     """
 
     def __init__(self, variant: int, units: int, heads: int, d: int, log_len: int,
@@ -196,6 +197,9 @@ class DecodeState:
             self.log_g = self._view(p.log_g, torch.float32, gshape)
             self.log_beta = (self._view(p.log_beta, torch.float32, (U, H, L))
                              if variant != DL_RWKV6 else None)
+            nt = L * (L - 1) // 2
+            self.log_t = (self._view(p.log_t, torch.float32, (U, H, nt))
+                          if variant != DL_RWKV6 and nt > 0 else None)
 
     def _view(self, ptr, dtype, shape):
         torch = self.torch

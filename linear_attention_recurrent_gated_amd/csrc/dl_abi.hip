@@ -38,7 +38,7 @@ dl_status ok() {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-    size_t off_flags, off_fill, off_base, off_k, off_v, off_g, off_b, total;
+    size_t off_flags, off_fill, off_base, off_k, off_v, off_g, off_b, off_t, total;
 };
 
 dl_status check_desc(const dl_desc *d) {
@@ -85,6 +85,8 @@ Layout layout_of(const dl_desc &d) {
     off = align256(off + pairs * L * gch * 4);
     l.off_b = off;
     off = align256(off + (d.variant == DL_RWKV6 ? 0 : pairs * L * 4));
+    l.off_t = off;
+    off = align256(off + pairs * (size_t)dl::packed_t_len(d.variant, d.log_len) * 4);
     l.total = off;
     return l;
 }
@@ -128,12 +130,11 @@ dl_status check_step_args(const dl_state *st, int32_t rows, const int32_t *slot_
 }
 
 // The step/readout kernels stage the key side of the log (keys, decays,
-// betas) in LDS; the request must fit the current device's per-workgroup
-// LDS (160 KiB on gfx950).
+// betas, key-side factors) in LDS; the request must fit the current
+// device's per-workgroup LDS (160 KiB on gfx950).
 dl_status check_lds(const dl_state *st) {
     const int es = st->desc.in_dtype == DL_BF16 ? 2 : 4;
-    const dl::LdsPlan lp = dl::lds_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len,
-                                        st->desc.log_len, false);
+    const dl::StepPlan lp = dl::step_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len);
     if (lp.bytes <= 65536)
         return DL_OK;
     int dev = 0, max_lds = 0;
@@ -209,6 +210,9 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.log_g = has_log ? reinterpret_cast<float *>(m + l.off_g) : nullptr;
     p.log_beta = (has_log && desc->variant != DL_RWKV6) ? reinterpret_cast<float *>(m + l.off_b)
                                                         : nullptr;
+    p.log_t = dl::packed_t_len(desc->variant, desc->log_len) > 0
+                  ? reinterpret_cast<float *>(m + l.off_t)
+                  : nullptr;
     const hipError_t e = dl::launch_zero(dev_mem, l.total,
                                          dl::Launch{static_cast<hipStream_t>(stream), nullptr, nullptr});
     if (e != hipSuccess) {
@@ -232,6 +236,7 @@ dl_status dl_state_view(const dl_state *st, dl_state_ptrs *out) {
     out->log_v = st->p.log_v;
     out->log_g = st->p.log_g;
     out->log_beta = st->p.log_beta;
+    out->log_t = st->p.log_t;
     out->fill = st->p.fill;
     out->flags = st->p.flags;
     return ok();

@@ -29,6 +29,7 @@ struct Params {
     void *log_v;
     float *log_g;
     float *log_beta;
+    float *log_t;      // packed columns of the compact-WY factor R (delta-rule variants)
     int *fill;
     int *flags;
 };
@@ -94,6 +95,17 @@ __device__ __forceinline__ float sum8(float x) {
     return x;
 }
 
+// Sum over all 64 lanes, returned as a wave-uniform value: the 8-lane
+// butterfly, a 16-lane mirror, then row_bcast15 / row_bcast31 (rows 1 and 3
+// add row 0 and 2; rows 2 and 3 add row 1) leave the total in lane 63.
+__device__ __forceinline__ float wave_sum(float x) {
+    x = sum8(x);
+    x += dpp_mov<0x140>(x);   // row_mirror
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // ---------------------------------------------------------------------------
 // LDS carve-up for staged log entries (step, readout and merge kernels).
 // k entries in the input dtype, decays already exponentiated (alpha), betas.
@@ -121,6 +133,161 @@ __host__ __device__ inline LdsPlan lds_plan(int variant, int D, int esize, int e
     return p;
 }
 
+// Orders this wave's LDS stores before its later LDS loads of other lanes'
+// data.  A wave's LDS instructions execute in issue order, so the fences
+// (wavefront scope, no instructions) only stop the compiler from moving
+// memory accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------------------
+// Key side of the DeltaLog step (dl_step.hip).
+//
+// Chunk layout: lane l covers the eight key channels 8 (l % G) .. + 7 of the
+// rows RP u + l / G (u < NU) of a pass over 16 logged entries.
+// ---------------------------------------------------------------------------
+template <int D>
+struct KeyLayout {
+    static constexpr int G = D / 8;      // lanes across one row
+    static constexpr int RP = 64 / G;    // rows per lane step
+    static constexpr int NU = 16 / RP;   // lane steps per 16-row pass
+};
+
+// LDS carve-up of the step kernel.  The staging regions are whole multiples
+// of one wave's direct-to-LDS load (64 lanes x 16 or 4 bytes).
+struct StepPlan {
+    int off_k;     // staged keys, rows of D elements in the input dtype
+    int off_lam;   // staged cumulative log-decays, rows of D floats (per-key decays)
+    int off_t;     // staged columns of R, packed
+    int off_r, off_u, off_f, off_l;   // per-entry scalars, 64 floats each
+    int off_c, off_e;                 // per-wave coefficients, 4 x 64 floats each
+    int off_qin;   // q as floats, D
+    int off_q;     // q0, D floats
+    int bytes;
+};
+
+__host__ __device__ inline int packed_t_len(int variant, int L) {
+    return variant == DL_RWKV6 ? 0 : L * (L - 1) / 2;
+}
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+__host__ __device__ inline StepPlan step_plan(int variant, int D, int esize, int L) {
+    StepPlan p;
+    p.off_k = 0;
+    p.off_lam = round_up(L * D * esize, 1024);
+    p.off_t = p.off_lam + (variant == DL_GDN ? 0 : round_up(L * D * 4, 1024));
+    p.off_r = p.off_t + round_up(packed_t_len(variant, L) * 4, 256);
+    p.off_u = p.off_r + 256;
+    p.off_f = p.off_u + 256;
+    p.off_l = p.off_f + 256;
+    p.off_c = p.off_l + 256;
+    p.off_e = p.off_c + 4 * 256;
+    p.off_qin = p.off_e + 4 * 256;
+    p.off_q = p.off_qin + D * 4;
+    p.bytes = p.off_q + D * 4;
+    return p;
+}
+
+// e^x through the hardware base-2 exponential: about 1 ulp plus the rounding
+// of x log2(e) (relative error near |x| 2^-24); results below the normal
+// range flush to zero.
+__device__ __forceinline__ float fast_exp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// Eight consecutive elements as floats (global memory or LDS).
+template <typename T>
+__device__ __forceinline__ void load8(const T *p, float *x) {
+    if constexpr (sizeof(T) == 4) {
+        const float4 a = reinterpret_cast<const float4 *>(p)[0];
+        const float4 b = reinterpret_cast<const float4 *>(p)[1];
+        x[0] = a.x, x[1] = a.y, x[2] = a.z, x[3] = a.w;
+        x[4] = b.x, x[5] = b.y, x[6] = b.z, x[7] = b.w;
+    } else {
+        const uint4 u = *reinterpret_cast<const uint4 *>(p);
+        x[0] = bf16_lo(u.x), x[1] = bf16_hi(u.x), x[2] = bf16_lo(u.y), x[3] = bf16_hi(u.y);
+        x[4] = bf16_lo(u.z), x[5] = bf16_hi(u.z), x[6] = bf16_lo(u.w), x[7] = bf16_hi(u.w);
+    }
+}
+
+// Stores eight floats that were widened from T (so the bf16 narrowing is exact).
+template <typename T>
+__device__ __forceinline__ void store8(T *p, const float *x) {
+    if constexpr (sizeof(T) == 4) {
+        reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+        reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+    } else {
+        uint4 u;
+        u.x = (__float_as_uint(x[0]) >> 16) | (__float_as_uint(x[1]) & 0xffff0000u);
+        u.y = (__float_as_uint(x[2]) >> 16) | (__float_as_uint(x[3]) & 0xffff0000u);
+        u.z = (__float_as_uint(x[4]) >> 16) | (__float_as_uint(x[5]) & 0xffff0000u);
+        u.w = (__float_as_uint(x[6]) >> 16) | (__float_as_uint(x[7]) & 0xffff0000u);
+        *reinterpret_cast<uint4 *>(p) = u;
+    }
+}
+
+// Sum over aligned groups of G lanes, G = 8 or 16 (every lane gets its group's sum).
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    x = sum8(x);
+    if constexpr (G == 16)
+        x += dpp_mov<0x140>(x);   // row_mirror
+    return x;
+}
+
+// x(l) + x(l ^ 16) and x(l) + x(l ^ 32): the gfx950 permlane swaps hand each
+// lane its partner's value alongside its own.
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the lanes l, l ^ G, l ^ 2G, ... (G = 8 or 16): the lanes that
+// share a channel group in the chunk layout.
+template <int G>
+__device__ __forceinline__ float cross_sum(float x) {
+    if constexpr (G == 8)
+        x += dpp_mov<0x128>(x);   // row_ror:8
+    return xor32_sum(xor16_sum(x));
+}
+
+// Sum over the lanes that share l % M (M = 2 or 4): rotations inside each
+// 16-lane row, then the permlane swaps across rows.
+template <int M>
+__device__ __forceinline__ float sum_mod(float x) {
+    static_assert(M == 2 || M == 4, "M = 2 or 4");
+    if constexpr (M == 2)
+        x += dpp_mov<0x122>(x);   // row_ror:2
+    x += dpp_mov<0x124>(x);       // row_ror:4
+    x += dpp_mov<0x128>(x);       // row_ror:8
+    return xor32_sum(xor16_sum(x));
+}
+
+// One wave's direct global -> LDS load of 16 (or 4) bytes per lane: lane l's
+// bytes land at lds + l * SIZE; lanes outside EXEC load and write nothing.
+// `lds` must be wave-uniform.
+template <int SIZE>
+__device__ __forceinline__ void load_to_lds(const void *src, unsigned char *lds) {
+    static_assert(SIZE == 16 || SIZE == 4, "16- or 4-byte loads");
+    auto *dst = (__attribute__((address_space(3))) void *)lds;
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(0), leaving the other counters free (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14 zero, expcnt 6:4 and lgkmcnt 11:8 at their maxima).
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Raise a device flag and poison a row's outputs (a rejected row).
 __device__ __forceinline__ void reject_row(const Params &P, float *orow, int D, int flag) {
     if (orow)
@@ -131,8 +298,8 @@ __device__ __forceinline__ void reject_row(const Params &P, float *orow, int D, 
 }
 
 // ---------------------------------------------------------------------------
-// staging of logged entries into LDS (keys in input dtype, exp'd decays,
-// betas; values optional).  Entries j0..j0+n-1 of `pair` go to LDS rows 0..n-1.
+// staging of logged entries into LDS (keys in input dtype, per-entry decays
+// alpha_j, betas; values optional).  Entries j0..j0+n-1 of `pair` go to LDS rows 0..n-1.
 // ---------------------------------------------------------------------------
 template <int V, int D, typename T, bool WITH_V>
 __device__ __forceinline__ void stage_entries(const Params &P, size_t pair, int j0, int n,
@@ -147,11 +314,15 @@ __device__ __forceinline__ void stage_entries(const Params &P, size_t pair, int 
             dst[i] = src[i];
     }
     {
+        // the log keeps the decay accumulated since its first entry:
+        // alpha_j = exp(Lam_j - Lam_{j-1}), Lam_{-1} = 0
         constexpr int ACH = (V == GDN) ? 1 : D;
         const float *src = P.log_g + e0 * ACH;
         float *dst = reinterpret_cast<float *>(smem + lp.off_a);
-        for (int i = tid; i < n * ACH; i += 256)
-            dst[i] = expf(src[i]);
+        for (int i = tid; i < n * ACH; i += 256) {
+            const float prev = (j0 * ACH + i >= ACH) ? src[i - ACH] : 0.f;
+            dst[i] = expf(src[i] - prev);
+        }
     }
     if constexpr (V != RWKV6) {
         float *dst = reinterpret_cast<float *>(smem + lp.off_b);

@@ -210,40 +210,38 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
         }
         __syncthreads();   // the previous chunk's LDS operands are consumed
 
-        // ---- phase 1a: raw keys and log-decays of the chunk into LDS (zeros past cnt)
+        // ---- phase 1: keys of the chunk (zeros past cnt) and the decay
+        //      accumulated since the chunk's start, Lam_j - Lam_{j0-1} (the log
+        //      stores Lam since its first entry; entries past cnt repeat the
+        //      last one, so their decay adds nothing)
         for (int idx = tid; idx < C * (D / 4); idx += 256) {
             const int j = idx / (D / 4), c = 4 * (idx - j * (D / 4));
             const int e = j0 + (j < cnt ? j : cnt - 1);
             float4 kv = Elem<T>::load4(Kl + (size_t)e * D + c);
-            float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if constexpr (V != GDN)
-                gv = *reinterpret_cast<const float4 *>(Gl + (size_t)e * D + c);
-            if (j >= cnt) {
-                kv = make_float4(0.f, 0.f, 0.f, 0.f);
-                gv = kv;
+            float4 lv, lb = make_float4(0.f, 0.f, 0.f, 0.f);
+            if constexpr (V == GDN) {
+                lv = make_float4(Gl[e], Gl[e], Gl[e], Gl[e]);
+                if (j0 > 0)
+                    lb = make_float4(Gl[j0 - 1], Gl[j0 - 1], Gl[j0 - 1], Gl[j0 - 1]);
+            } else {
+                lv = *reinterpret_cast<const float4 *>(Gl + (size_t)e * D + c);
+                if (j0 > 0)
+                    lb = *reinterpret_cast<const float4 *>(Gl + (size_t)(j0 - 1) * D + c);
             }
+            if (j >= cnt)
+                kv = make_float4(0.f, 0.f, 0.f, 0.f);
+            const float4 lam = make_float4(lv.x - lb.x, lv.y - lb.y, lv.z - lb.z, lv.w - lb.w);
             *reinterpret_cast<float4 *>(&sK[j * KS + c]) = kv;
-            if constexpr (V != GDN)
-                *reinterpret_cast<float4 *>(&sLam[j * KS + c]) = gv;
+            *reinterpret_cast<float4 *>(&sLam[j * KS + c]) = lam;
+            *reinterpret_cast<float4 *>(&sKt[j * KS + c]) =
+                make_float4(kv.x * expf(lam.x), kv.y * expf(lam.y), kv.z * expf(lam.z), kv.w * expf(lam.w));
+            if (j == C - 1)
+                *reinterpret_cast<float4 *>(&sELC[c]) =
+                    make_float4(expf(lam.x), expf(lam.y), expf(lam.z), expf(lam.w));
         }
         if (tid < C) {
             const int e = j0 + (tid < cnt ? tid : cnt - 1);
             sB[tid] = (V != RWKV6 && tid < cnt) ? Bl[e] : 0.f;
-            if constexpr (V == GDN)
-                sM[tid] = (tid < cnt) ? Gl[e] : 0.f;      // scratch: scalar log-decays
-        }
-        __syncthreads();
-        // ---- phase 1b: thread c accumulates the decay of key channel c through the chunk
-        if (tid < D) {
-            const int c = tid;
-            float lam = 0.f;
-            for (int j = 0; j < C; ++j) {
-                lam += (V == GDN) ? sM[j] : sLam[j * KS + c];
-                const float kr = sK[j * KS + c];
-                sKt[j * KS + c] = kr * expf(lam);
-                sLam[j * KS + c] = lam;
-            }
-            sELC[c] = expf(lam);
         }
         __syncthreads();
 

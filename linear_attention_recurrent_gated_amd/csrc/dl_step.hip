@@ -156,116 +156,82 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
     }
 }
 
-// One pull-back of the query through logged transform j (lane columns only).
-// Returns coef_j; the dot ends in the 8-lane butterfly so every group agrees.
-template <int V, int D>
-__device__ __forceinline__ float pull_back(float *qv, const float *kj, const float *aj,
-                                           float a_scalar, float bj) {
-    using SH = Shape<D>;
-    float d = 0.f;
-#pragma unroll
-    for (int f = 0; f < SH::FPL; ++f)
-        d += kj[f] * qv[f];
-    d = sum8(d);
-    const float coef = (V == RWKV6) ? d : bj * d;
-#pragma unroll
-    for (int f = 0; f < SH::FPL; ++f) {
-        const float a = (V == GDN) ? a_scalar : aj[f];
-        qv[f] = (V == RWKV6) ? a * qv[f] : a * (qv[f] - coef * kj[f]);
-    }
-    return coef;
-}
+// ---------------------------------------------------------------------------
+// DeltaLog step / readout.
+//
+// The log holds entries j = 0..c (the newest last) with Lam_j, the log-decay
+// accumulated from the first entry through entry j (stored cumulative).
+// With E_j = exp(Lam_j), D(j, i) = exp(Lam_i - Lam_j) and R = (I + N)^{-1}
+// for the couplings N_ij = beta_i k_i.(D(i, j) k_j) (i < j), the pending
+// transforms pull q back in compact WY form:
+//   r_j   = beta_j k_j.(D(j, c) q)           (additive variant: beta = 1)
+//   coef  = R r                              (additive: coef = r)
+//   q0    = E_c q - sum_j coef_j E_j k_j     (additive: no k terms)
+//   o     = S0 q0 + sum_j coef_j v_j
+// which equals pulling q back through the transforms one at a time, newest
+// first (coef_j = beta_j k_j.q_j, q_{j-1} = alpha_j (q_j - coef_j k_j)),
+// without that chain of dependent steps.  R gains one column per appended
+// entry, R[:n, n] = -R[:n, :n] N[:n, n], kept in the log beside the keys:
+// key-side factors computed once per slot and head, as the DeltaLog page's
+// Kernel Implementation describes.
+//
+// One workgroup of four waves per (row, head).  Every wave holds D/4 rows of
+// S0 in registers (loads issued first) and takes a quarter of the key side:
+// the dot products and q0 run in the chunk layout (eight channels of one
+// entry per lane, DPP / permlane reductions), R r with one entry per lane
+// (each wave computes it for itself, so no barrier separates it from q0).
+// ---------------------------------------------------------------------------
 
-// ---------------------------------------------------------------------------
-// Key-side staging for the chain, done by one wave: logged keys (input
-// dtype), alpha = exp(g) and beta of entries [0, n) into LDS.  Loads use
-// clamped in-range addresses so that a batch issues without branches and
-// waits only once.
-// ---------------------------------------------------------------------------
+// This wave's share of the staging of entries [0, n) of `pair` into LDS
+// (direct-to-LDS loads, every fourth batch of 64 lanes): keys, cumulative
+// log-decays (per-key decays) and the packed R columns.  Lanes past the last
+// element are masked off, so nothing is written past entry n - 1.
 template <int V, int D, typename T>
-__device__ __forceinline__ void stage_key_side(const Params &P, size_t pair, int n,
-                                               unsigned char *smem, const LdsPlan &lp, int lane) {
-    constexpr int B = 8;
-    // An empty log reads nothing: a state without a log (L = 0) has no log
-    // arrays at all, so even the clamped loads below must not run.
-    if (n <= 0)
-        return;
+__device__ __forceinline__ void stage_log(const Params &P, size_t pair, int n, unsigned char *smem,
+                                          const StepPlan &sp, int lane, int wave) {
     const size_t e0 = pair * P.L;
-    float *sa = reinterpret_cast<float *>(smem + lp.off_a);
-    float *sb = reinterpret_cast<float *>(smem + lp.off_b);
-    const int nl = n;
-    // scalar decays and betas: one entry per lane (n <= 64)
-    float gs = 0.f, bs = 0.f;
-    if constexpr (V == GDN)
-        gs = P.log_g[e0 + (lane < nl ? lane : nl - 1)];
-    if constexpr (V != RWKV6)
-        bs = P.log_beta[e0 + (lane < nl ? lane : nl - 1)];
-    // keys: n * D * sizeof(T) contiguous bytes
-    const int nk = n * D * (int)sizeof(T) / 16;
-    const uint4 *ksrc = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_k) + e0 * D);
-    uint4 *kdst = reinterpret_cast<uint4 *>(smem + lp.off_k);
-    for (int base = 0; base < nk; base += 64 * B) {
-        uint4 tmp[B];
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            const int idx = base + u * 64 + lane;
-            tmp[u] = ksrc[idx < nk ? idx : nk - 1];
-        }
-#pragma unroll
-        for (int u = 0; u < B; ++u) {
-            const int idx = base + u * 64 + lane;
-            if (idx < nk)
-                kdst[idx] = tmp[u];
-        }
+    constexpr int CPR = D * (int)sizeof(T) / 16;
+    const int nk = n * CPR;
+    const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_k) + e0 * D);
+    for (int b = 64 * wave; b < nk; b += 256) {
+        const int idx = b + lane;
+        if (idx < nk)
+            load_to_lds<16>(ks + idx, smem + sp.off_k + 16 * b);
     }
     if constexpr (V != GDN) {
-        const int ng = n * D / 4;
-        const float4 *gsrc = reinterpret_cast<const float4 *>(P.log_g + e0 * D);
-        float4 *gdst = reinterpret_cast<float4 *>(sa);
-        for (int base = 0; base < ng; base += 64 * B) {
-            float4 tmp[B];
-#pragma unroll
-            for (int u = 0; u < B; ++u) {
-                const int idx = base + u * 64 + lane;
-                tmp[u] = gsrc[idx < ng ? idx : ng - 1];
-            }
-#pragma unroll
-            for (int u = 0; u < B; ++u) {
-                const int idx = base + u * 64 + lane;
-                if (idx < ng)
-                    gdst[idx] = make_float4(expf(tmp[u].x), expf(tmp[u].y), expf(tmp[u].z), expf(tmp[u].w));
-            }
+        const int nl = n * (D / 4);
+        const float4 *ls = reinterpret_cast<const float4 *>(P.log_g + e0 * D);
+        for (int b = 64 * wave; b < nl; b += 256) {
+            const int idx = b + lane;
+            if (idx < nl)
+                load_to_lds<16>(ls + idx, smem + sp.off_lam + 16 * b);
         }
     }
-    if (lane < n) {
-        if constexpr (V == GDN)
-            sa[lane] = expf(gs);
-        if constexpr (V != RWKV6)
-            sb[lane] = bs;
+    if constexpr (V != RWKV6) {
+        const int nt = n * (n - 1) / 2;
+        const float *ts = P.log_t + pair * packed_t_len(V, P.L);
+        for (int b = 64 * wave; b < nt; b += 256) {
+            const int idx = b + lane;
+            if (idx < nt)
+                load_to_lds<4>(ts + idx, smem + sp.off_t + 4 * b);
+        }
     }
 }
 
-// ---------------------------------------------------------------------------
-// DeltaLog step (APPEND) / readout (!APPEND).  Five waves per (unit, head):
-// wave 0 is the key side (stages the logged keys and decays, pulls q back
-// through them -- computed once and shared by all value rows); waves 1..4
-// each own D/4 value rows of the base, whose loads they issue before
-// anything else, and do the append.
-// MV: value-log entries each lane reads per row (entries s, s+8, ...).
-// ---------------------------------------------------------------------------
 template <int V, int D, typename T, bool APPEND, int MV>
-__global__ void __launch_bounds__(320)
+__global__ void __launch_bounds__(256)
 log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                 const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
                 const float *__restrict__ beta, float *__restrict__ o) {
     using SH = Shape<D>;
+    using KL = KeyLayout<D>;
+    constexpr int G = KL::G, RP = KL::RP, PASS = 4 * RP;   // entries per pass of the four waves
+    constexpr bool DELTA = V != RWKV6;
     extern __shared__ __align__(16) unsigned char smem[];
     const int H = P.heads, L = P.L;
     const int pr = blockIdx.x;
     const int r = pr / H, h = pr - r * H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int grp = lane >> 3, s = lane & 7;
-    const int vw = wave - 1;                         // value wave index
     float *orow = o + (size_t)pr * D;
 
     const int unit = slot_idx ? slot_idx[r] : r;
@@ -275,134 +241,293 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
     }
     const size_t pair = (size_t)unit * H + h;
     const size_t io = (size_t)pr * D;
-    const int n = P.fill[pair];                      // entries already logged
+    const size_t e0 = pair * L;
+    const StepPlan sp = step_plan(V, D, (int)sizeof(T), L);
+    float *slam = reinterpret_cast<float *>(smem + sp.off_lam);
+    const float *sT = reinterpret_cast<const float *>(smem + sp.off_t);
+    float *sr = reinterpret_cast<float *>(smem + sp.off_r);
+    float *su = reinterpret_cast<float *>(smem + sp.off_u);
+    float *sf = reinterpret_cast<float *>(smem + sp.off_f);
+    float *sl = reinterpret_cast<float *>(smem + sp.off_l);
+    float *sc = reinterpret_cast<float *>(smem + sp.off_c) + 64 * wave;
+    float *se = reinterpret_cast<float *>(smem + sp.off_e) + 64 * wave;
+    float *sq = reinterpret_cast<float *>(smem + sp.off_q);
+    float *sqin = reinterpret_cast<float *>(smem + sp.off_qin);
+    auto krow = [&](int j) { return reinterpret_cast<T *>(smem + sp.off_k) + j * D; };
+
+    // ---- loads that need nothing: fill, this wave's rows of S0, the inputs
+    const int n = P.fill[pair];
+    const int grp = lane >> 3, s = lane & 7;
     const float *Sp = P.base + pair * D * D;
     float4 st[SH::ITER][SH::NCH];
-    if (wave > 0) {
 #pragma unroll
-        for (int it = 0; it < SH::ITER; ++it) {
-            const int row = vw * SH::RPW + it * 8 + grp;
+    for (int it = 0; it < SH::ITER; ++it) {
+        const int row = wave * SH::RPW + it * 8 + grp;
 #pragma unroll
-            for (int m = 0; m < SH::NCH; ++m)
-                st[it][m] = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + col_of(s, m, 0));
-        }
+        for (int m = 0; m < SH::NCH; ++m)
+            st[it][m] = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
+    const int cg = lane % G, ro = lane / G, ch0 = 8 * cg;
+    float qv[8], kn[8];
+    load8<T>(q + io + ch0, qv);
+    if constexpr (APPEND)
+        load8<T>(k + io + ch0, kn);
     __builtin_amdgcn_sched_barrier(0);
     if (APPEND ? (n >= L || n < 0) : (n > L || n < 0)) {
         reject_row(P, orow, D, DL_FLAG_LOG_FULL);
         return;
     }
-    const LdsPlan lp = lds_plan(V, D, (int)sizeof(T), L, L, false);
-    float *sq = reinterpret_cast<float *>(smem + lp.off_q);
-    float *sc = reinterpret_cast<float *>(smem + lp.off_c);
+
+    // ---- loads that need n: logged values of this wave's rows (clamped,
+    //      branch-free; an empty log reads a dummy in-range address instead),
+    //      the staging, and (wave 0) the per-entry scalars and the append
     float vl[SH::ITER][MV];
     float vc[SH::ITER];
-
-    if (wave == 0) {
-        // ---- key side: pull q back through every logged transform, newest first
-        float qv[SH::FPL], kj[SH::FPL], aj[SH::FPL];
-        float a_s = 1.f, bj = 1.f;
-#pragma unroll
-        for (int m = 0; m < SH::NCH; ++m) {
-            f4_to(qv + 4 * m, Elem<T>::load4(q + io + col_of(s, m, 0)));
-            if constexpr (APPEND) {
-                f4_to(kj + 4 * m, Elem<T>::load4(k + io + col_of(s, m, 0)));
-                if constexpr (V != GDN)
-                    f4_to(aj + 4 * m, *reinterpret_cast<const float4 *>(g + io + col_of(s, m, 0)));
-            }
-        }
-        if constexpr (APPEND) {
-            if constexpr (V == GDN)
-                a_s = g[pr];
-            if constexpr (V != RWKV6)
-                bj = beta[pr];
-        }
-        stage_key_side<V, D, T>(P, pair, n, smem, lp, lane);
-        if constexpr (APPEND) {
-            if constexpr (V == GDN) {
-                a_s = expf(a_s);
-            } else {
-#pragma unroll
-                for (int f = 0; f < SH::FPL; ++f)
-                    aj[f] = expf(aj[f]);
-            }
-            const float coef = pull_back<V, D>(qv, kj, aj, a_s, bj);
-            if (lane == 0)
-                sc[n] = coef;
-        }
-        const unsigned char *sk = smem + lp.off_k;
-        const float *sa = reinterpret_cast<const float *>(smem + lp.off_a);
-        const float *sb = reinterpret_cast<const float *>(smem + lp.off_b);
-        for (int j = n - 1; j >= 0; --j) {
-#pragma unroll
-            for (int m = 0; m < SH::NCH; ++m) {
-                f4_to(kj + 4 * m, lds_load4<T>(sk, j * D + col_of(s, m, 0)));
-                if constexpr (V != GDN)
-                    f4_to(aj + 4 * m, *reinterpret_cast<const float4 *>(sa + j * D + col_of(s, m, 0)));
-            }
-            if constexpr (V == GDN)
-                a_s = sa[j];
-            if constexpr (V != RWKV6)
-                bj = sb[j];
-            const float coef = pull_back<V, D>(qv, kj, aj, a_s, bj);
-            if (lane == 0)
-                sc[j] = coef;
-        }
-        if (grp == 0) {
-#pragma unroll
-            for (int m = 0; m < SH::NCH; ++m)
-                *reinterpret_cast<float4 *>(sq + col_of(s, m, 0)) =
-                    make_float4(qv[4 * m], qv[4 * m + 1], qv[4 * m + 2], qv[4 * m + 3]);
-        }
-    } else {
-        // ---- value side: logged values of this lane's rows (clamped, branch-free
-        //      loads; none at all for an empty log, whose arrays may not exist)
-        const T *Vp = static_cast<const T *>(P.log_v) + pair * L * D;
-        const int nl = n - 1;
+    {
+        const T *Vp = (n > 0) ? static_cast<const T *>(P.log_v) + e0 * D
+                              : reinterpret_cast<const T *>(P.base);
+        const int nl = n > 0 ? n - 1 : 0;
 #pragma unroll
         for (int it = 0; it < SH::ITER; ++it) {
-            const int row = vw * SH::RPW + it * 8 + grp;
+            const int row = wave * SH::RPW + it * 8 + grp;
 #pragma unroll
-            for (int mm = 0; mm < MV; ++mm)
-                vl[it][mm] = 0.f;
-            if (n > 0) {
-#pragma unroll
-                for (int mm = 0; mm < MV; ++mm) {
-                    const int j = s + 8 * mm;
-                    const float x = Elem<T>::load1(Vp + (size_t)(j < n ? j : nl) * D + row);
-                    vl[it][mm] = (j < n) ? x : 0.f;
-                }
+            for (int mm = 0; mm < MV; ++mm) {
+                const int j = s + 8 * mm;
+                const float x = Elem<T>::load1(Vp + (size_t)(j < n ? j : nl) * D + row);
+                vl[it][mm] = (j < n) ? x : 0.f;
             }
             vc[it] = APPEND ? Elem<T>::load1(v + io + row) : 0.f;
         }
+    }
+    if (n > 0)
+        stage_log<V, D, T>(P, pair, n, smem, sp, lane, wave);
+    if (wave == 0) {
+        const int jl = lane < n ? lane : (n > 0 ? n - 1 : 0);
+        float lam_j = 0.f, b_j = 1.f;     // entry `lane`: Lam (GDN) and beta
+        float lc[8];                      // Lam_c on this lane's channels (per-key decays)
+        float g_s = 0.f, b_in = 1.f, gn[8], vv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            lc[i] = 0.f;
+        if (n > 0) {
+            if constexpr (V == GDN)
+                lam_j = P.log_g[e0 + jl];
+            if constexpr (DELTA)
+                b_j = P.log_beta[e0 + jl];
+            if constexpr (V != GDN)
+                load8<float>(P.log_g + (e0 + n - 1) * D + ch0, lc);
+        }
         if constexpr (APPEND) {
-            // append (k, v, g, beta) at slot n: bit copies of the inputs
-            const int t = tid - 64;
-            const size_t e = pair * L + n;
-            T *lk = static_cast<T *>(P.log_k) + e * D;
-            T *lv = static_cast<T *>(P.log_v) + e * D;
-            for (int i = t; i < D; i += 256) {
-                lk[i] = k[io + i];
-                lv[i] = v[io + i];
+            load8<T>(v + io + ch0, vv);
+            if constexpr (V == GDN)
+                g_s = g[pr];
+            else
+                load8<float>(g + io + ch0, gn);
+            if constexpr (DELTA)
+                b_in = beta[pr];
+        }
+        // Lam_c, then the append of entry n: bit copies of k and v, the decay
+        // accumulated through it, beta
+        float lam_c = 0.f;
+        if constexpr (V == GDN) {
+            const float prev = n > 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_j), n - 1)) : 0.f;
+            lam_c = APPEND ? prev + g_s : prev;
+        } else if constexpr (APPEND) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                lc[i] += gn[i];
+        }
+        if constexpr (APPEND) {
+            const size_t e = e0 + n;
+            if (ro == 0) {
+                store8<T>(static_cast<T *>(P.log_k) + e * D + ch0, kn);
+                store8<T>(static_cast<T *>(P.log_v) + e * D + ch0, vv);
+                store8<T>(krow(n) + ch0, kn);
+                if constexpr (V != GDN) {
+                    store8<float>(P.log_g + e * D + ch0, lc);
+                    store8<float>(slam + n * D + ch0, lc);
+                }
             }
+            if (lane == 0) {
+                if constexpr (V == GDN)
+                    P.log_g[e] = lam_c;
+                if constexpr (DELTA)
+                    P.log_beta[e] = b_in;
+            }
+            if (lane == n) {
+                lam_j = lam_c;
+                b_j = b_in;
+            }
+        }
+        // per-entry factor of the dot products: beta_j (GDN: times D(j, c)),
+        // and (GDN) Lam_j for the other waves
+        const int ct = APPEND ? n + 1 : n;
+        if (lane < ct) {
+            float f = b_j;
             if constexpr (V == GDN) {
-                if (t == 0)
-                    P.log_g[e] = g[pr];
-            } else {
-                for (int i = t; i < D; i += 256)
-                    P.log_g[e * D + i] = g[io + i];
+                f *= fast_exp(lam_c - lam_j);
+                sl[lane] = lam_j;
             }
-            if constexpr (V != RWKV6) {
-                if (t == 0)
-                    P.log_beta[e] = beta[pr];
+            sf[lane] = f;
+        }
+        if (ro == 0)
+            store8<float>(sqin + ch0, qv);
+    }
+    wait_vm_all();      // this wave's staging (and everything before it) has landed
+    __syncthreads();    // 1: staged entries, the new entry, per-entry factors
+
+    const int ct = APPEND ? n + 1 : n;   // entries the readout sees
+    const int npass = (ct + PASS - 1) / PASS;
+    float lam_c = 0.f, lc[8];
+    if constexpr (V == GDN) {
+        lam_c = ct > 0 ? sl[ct - 1] : 0.f;
+    } else {
+        if (ct > 0)
+            load8<float>(slam + (ct - 1) * D + ch0, lc);
+        else
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                lc[i] = 0.f;
+    }
+
+    // ---- r_j = f_j k_j.(D q) and, for the appended entry, u_j = f_j k_j.(D k_n)
+    //      (the decays D(j, c) inside the dot for the per-key variants); this
+    //      wave's entries of each pass
+    for (int p = 0; p < npass; ++p) {
+        const int j = PASS * p + RP * wave + ro;
+        const int jc = j < ct ? j : ct - 1;
+        float kr[8], lr[8];
+        load8<T>(krow(jc) + ch0, kr);
+        if constexpr (V != GDN)
+            load8<float>(slam + jc * D + ch0, lr);
+        const float fr = DELTA ? sf[jc] : 1.f;
+        float ar = 0.f, au = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float kd = kr[i];
+            if constexpr (V != GDN)
+                kd *= fast_exp(lc[i] - lr[i]);
+            ar += kd * qv[i];
+            if constexpr (APPEND && DELTA)
+                au += kd * kn[i];
+        }
+        ar = group_sum<G>(ar);
+        if constexpr (APPEND && DELTA)
+            au = group_sum<G>(au);
+        if (cg == 0 && j < ct) {
+            sr[j] = fr * ar;
+            if constexpr (APPEND && DELTA)
+                su[j] = fr * au;
+        }
+    }
+    __syncthreads();    // 2: r and u of every entry
+
+    // ---- lane i: the new column R[i, n] = -(u_i + sum_{i<m<n} R[i, m] u_m)
+    //      and coef_i = (R r)_i, sharing the loads of R (every wave for itself;
+    //      wave 0 stores the new column)
+    float coef = 0.f;
+    if (lane < ct) {
+        const int i = lane;
+        coef = sr[i];
+        if constexpr (DELTA) {
+            float acc_u = APPEND ? su[i] : 0.f;
+            const int mend = APPEND ? n : ct;     // stored columns m < mend
+            for (int m0 = 0; m0 < mend; m0 += 8) {
+                float rv[8], uv[8], Rv[8];
+#pragma unroll
+                for (int t = 0; t < 8; t += 4) {
+                    const float4 a = *reinterpret_cast<const float4 *>(sr + m0 + t);
+                    rv[t] = a.x, rv[t + 1] = a.y, rv[t + 2] = a.z, rv[t + 3] = a.w;
+                    if constexpr (APPEND) {
+                        const float4 b = *reinterpret_cast<const float4 *>(su + m0 + t);
+                        uv[t] = b.x, uv[t + 1] = b.y, uv[t + 2] = b.z, uv[t + 3] = b.w;
+                    }
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    const int m = m0 + t;
+                    // column m holds rows 0..m-1; other lanes read an in-range dummy
+                    const int lim = m < mend ? m : 0;
+                    const int col = m < mend ? m * (m - 1) / 2 : 0;
+                    Rv[t] = sT[col + (i < lim ? i : 0)];
+                    Rv[t] = i < lim ? Rv[t] : 0.f;
+                }
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    coef += Rv[t] * rv[t];
+                    if constexpr (APPEND)
+                        acc_u += Rv[t] * uv[t];
+                }
+            }
+            if constexpr (APPEND) {
+                if (i < n) {
+                    const float w = -acc_u;
+                    if (wave == 0)
+                        P.log_t[pair * packed_t_len(V, L) + n * (n - 1) / 2 + i] = w;
+                    coef += w * sr[n];
+                }
             }
         }
     }
-    __syncthreads();
-    if (wave == 0)
-        return;
+    if (lane < PASS * npass) {
+        sc[lane] = coef;                    // zero past the last entry
+        if constexpr (V == GDN)
+            se[lane] = lane < ct ? coef * fast_exp(sl[lane]) : 0.f;
+    }
+    wave_lds_sync();
 
-    // ---- value side: o = S0 q0 + sum_j coef_j v_j for this lane's rows
+    // ---- q0 = E_c q - sum_j coef_j E_j k_j on this wave's quarter of the
+    //      channels: lane l takes channels 8 (l % LQ) .. + 7 of the quarter for
+    //      the entries RQ p + l / LQ
+    {
+        constexpr int LQ = D / 32, RQ = 64 / LQ;   // lanes across the quarter, entries per step
+        const int c4 = lane % LQ, jr = lane / LQ;
+        const int chq = (D / 4) * wave + 8 * c4;
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc[i] = 0.f;
+        if constexpr (DELTA) {
+            for (int p = 0; p < ct; p += RQ) {
+                const int j = p + jr;
+                const int jc = j < ct ? j : ct - 1;
+                float kr[8], lr[8];
+                load8<T>(krow(jc) + chq, kr);
+                if constexpr (V != GDN)
+                    load8<float>(slam + jc * D + chq, lr);
+                const float cr = j < ct ? ((V == GDN) ? se[jc] : sc[jc]) : 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    float x = cr * kr[i];
+                    if constexpr (V != GDN)
+                        x *= fast_exp(lr[i]);
+                    acc[i] += x;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] = sum_mod<LQ>(acc[i]);
+        }
+        if (jr == 0) {
+            float qq[8], lq[8], out[8];
+            load8<float>(sqin + chq, qq);
+            if constexpr (V != GDN) {
+                if (ct > 0)
+                    load8<float>(slam + (ct - 1) * D + chq, lq);
+                else
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        lq[i] = 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                out[i] = fast_exp((V == GDN) ? lam_c : lq[i]) * qq[i] - acc[i];
+            store8<float>(sq + chq, out);
+        }
+    }
+    __syncthreads();    // 3: q0
+
+    // ---- o = S0 q0 + sum_j coef_j v_j for this wave's rows
     float qt[SH::FPL];
 #pragma unroll
     for (int m = 0; m < SH::NCH; ++m)
@@ -416,23 +541,23 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
     const float ccur = (APPEND && s == 0) ? sc[n] : 0.f;
 #pragma unroll
     for (int it = 0; it < SH::ITER; ++it) {
-        const int row = vw * SH::RPW + it * 8 + grp;
-        float acc = 0.f;
+        const int row = wave * SH::RPW + it * 8 + grp;
+        float acc_o = 0.f;
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m) {
-            acc += st[it][m].x * qt[4 * m] + st[it][m].y * qt[4 * m + 1] +
-                   st[it][m].z * qt[4 * m + 2] + st[it][m].w * qt[4 * m + 3];
+            acc_o += st[it][m].x * qt[4 * m] + st[it][m].y * qt[4 * m + 1] +
+                     st[it][m].z * qt[4 * m + 2] + st[it][m].w * qt[4 * m + 3];
         }
 #pragma unroll
         for (int mm = 0; mm < MV; ++mm)
-            acc += cf[mm] * vl[it][mm];
+            acc_o += cf[mm] * vl[it][mm];
         if (APPEND)
-            acc += ccur * vc[it];
-        acc = sum8(acc);
+            acc_o += ccur * vc[it];
+        acc_o = sum8(acc_o);
         if (s == 0)
-            orow[row] = acc;
+            orow[row] = acc_o;
     }
-    if (APPEND && tid == 64)
+    if (APPEND && tid == 0)
         P.fill[pair] = n + 1;
 }
 
@@ -476,14 +601,19 @@ template <int V, int D, typename T, bool APPEND>
 static hipError_t log_t(const Params &P, int rows, const int *slot_idx, const void *q,
                         const void *k, const void *v, const float *g, const float *beta,
                         float *o, const Launch &ln) {
-    const LdsPlan lp = lds_plan(V, D, (int)sizeof(T), P.L, P.L, false);
-    const dim3 grid(rows * P.heads), block(320);
+    const StepPlan sp = step_plan(V, D, (int)sizeof(T), P.L);
+    const dim3 grid(rows * P.heads), block(256);
+    // MV = value-log entries per lane per row = ceil(L / 8), rounded up to 2, 4 or 8
     if (P.L <= 16) {
-        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 2>), grid, block, lp.bytes, ln.stream, ln.start, ln.stop, 0,
+        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 2>), grid, block, sp.bytes, ln.stream, ln.start, ln.stop, 0,
+                           P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
+                           static_cast<const T *>(v), g, beta, o);
+    } else if (P.L <= 32) {
+        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 4>), grid, block, sp.bytes, ln.stream, ln.start, ln.stop, 0,
                            P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
                            static_cast<const T *>(v), g, beta, o);
     } else {
-        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 8>), grid, block, lp.bytes, ln.stream, ln.start, ln.stop, 0,
+        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 8>), grid, block, sp.bytes, ln.stream, ln.start, ln.stop, 0,
                            P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
                            static_cast<const T *>(v), g, beta, o);
     }

@@ -172,6 +172,94 @@ def qchain_readout(variant, base, log, q):
     return o
 
 
+def wy_t_column(variant, log, j):
+    """Coupling column ``N[:j, j]`` of logged entry j (0-based) to the earlier ones.
+
+    ``N_ij = beta_i sum_c k_i[c] k_j[c] D(i, j)[c]`` for ``i < j``: entry i's
+    coefficient depends on entry j's through it.  Appending entry j adds one
+    column to ``R = (I + N)^{-1}``: ``R[:j, j] = -R[:j, :j] N[:j, j]``,
+    ``R[j, j] = 1`` (see :func:`wy_build_r`).  The additive variant has no
+    coupling (``R = I``).
+    """
+    dk = len(log[0][0])
+    decays = [_chan(variant, e[2], dk) for e in log]
+
+    def D(i, jj):
+        out = [Fr(1)] * dk
+        for m in range(i + 1, jj + 1):
+            out = [x * y for x, y in zip(out, decays[m])]
+        return out
+
+    if variant == RWKV6:
+        return [Fr(0)] * j + [Fr(1)]
+    kj = [Fr(x) for x in log[j][0]]
+    u = []
+    for i in range(j):
+        ki = [Fr(x) for x in log[i][0]]
+        u.append(Fr(log[i][3]) * sum((a * b * c for a, b, c in zip(ki, kj, D(i, j))), Fr(0)))
+    return u
+
+
+def wy_build_r(variant, log):
+    """R = (I + N)^{-1} (upper triangular, unit diagonal) built one column per entry."""
+    n = len(log)
+    R = [[Fr(int(i == j)) for j in range(n)] for i in range(n)]
+    for j in range(1, n):
+        u = wy_t_column(variant, log, j)
+        if variant == RWKV6:
+            continue
+        for i in range(j):
+            R[i][j] = -sum((R[i][m] * u[m] for m in range(i, j)), Fr(0))
+    return R
+
+
+def wy_readout(variant, base, log, q):
+    """Readout of base + log in compact WY form, with no sequential chain.
+
+    With ``E_j`` the decay accumulated over entries ``0..j`` and
+    ``D(j, c)`` the decay of entries ``j+1..c`` (c the newest):
+    ``r_j = beta_j k_j . (D(j, c) * q)`` (additive: beta = 1),
+    ``coef = R r``, ``q0 = E_c * q - sum_j coef_j E_j * k_j`` (additive: no
+    k terms, ``coef = r``), and ``o = base q0 + sum_j coef_j v_j``.
+    """
+    n = len(log)
+    dk = len(q)
+    if n == 0:
+        return matvec(base, [Fr(x) for x in q])
+    decays = [_chan(variant, e[2], dk) for e in log]
+    E = []
+    acc = [Fr(1)] * dk
+    for a in decays:
+        acc = [x * y for x, y in zip(acc, a)]
+        E.append(acc)
+    c = n - 1
+
+    def D(j, i):
+        out = [Fr(1)] * dk
+        for m in range(j + 1, i + 1):
+            out = [x * y for x, y in zip(out, decays[m])]
+        return out
+
+    qf = [Fr(x) for x in q]
+    r = []
+    for j, (k, v, alpha, beta) in enumerate(log):
+        b = Fr(1) if variant == RWKV6 else Fr(beta)
+        r.append(b * sum((Fr(kk) * d * x for kk, d, x in zip(k, D(j, c), qf)), Fr(0)))
+    if variant == RWKV6:
+        coef = r
+        q0 = [e * x for e, x in zip(E[c], qf)]
+    else:
+        R = wy_build_r(variant, log)
+        coef = [sum((R[i][j] * r[j] for j in range(i, n)), Fr(0)) for i in range(n)]
+        q0 = [e * x for e, x in zip(E[c], qf)]
+        for j, (k, v, alpha, beta) in enumerate(log):
+            q0 = [x - coef[j] * ej * Fr(kk) for x, ej, kk in zip(q0, E[j], k)]
+    o = matvec(base, q0)
+    for j, (k, v, alpha, beta) in enumerate(log):
+        o = [x + coef[j] * Fr(vv) for x, vv in zip(o, v)]
+    return o
+
+
 def wy_merge(variant, base, log):
     """Materialise ``base`` followed by the logged updates in WY/UT form.
 

@@ -47,6 +47,7 @@ def _expected_bytes(variant, units, heads, d, L, es):
     total += _align(pairs * L * d * es) * 2
     total += _align(pairs * L * (1 if variant == B.DL_GDN else d) * 4)
     total += _align(0 if variant == B.DL_RWKV6 else pairs * L * 4)
+    total += _align(0 if variant == B.DL_RWKV6 else pairs * (L * (L - 1) // 2) * 4)
     return total
 
 

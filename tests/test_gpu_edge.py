@@ -37,7 +37,8 @@ def _bits(t):
 ])
 def test_schedule_and_payload_bit_exact(wl, L):
     """After every step: fill == (tokens so far) mod L for every head, and the
-    slot written holds bit copies of that step's k, v, g, beta."""
+    slot written holds bit copies of that step's k, v and beta, and the decay
+    accumulated through it."""
     first = W.first_active_step(wl, L)
     log(f"case schedule {wl.name} L={L} offsets={L - 1 - first}")
 
@@ -54,7 +55,12 @@ def test_schedule_and_payload_bit_exact(wl, L):
             slot = (m - 1) % L
             assert np.array_equal(_bits(st.log_k[b, :, slot]), _bits(to_torch(s.k[b], wl.dtype)))
             assert np.array_equal(_bits(st.log_v[b, :, slot]), _bits(to_torch(s.v[b], wl.dtype)))
-            assert np.array_equal(st.log_g[b, :, slot].cpu().numpy(), s.g[b])
+            # the log keeps the decay accumulated since its first entry, summed in
+            # fp32 in entry order
+            lam = np.zeros_like(s.g[b])
+            for tp in range(tau - slot, tau + 1):
+                lam = (lam + W.draw_step(wl, tp).g[b]).astype(np.float32)
+            assert np.array_equal(st.log_g[b, :, slot].cpu().numpy(), lam)
             if s.beta is not None:
                 assert np.array_equal(st.log_beta[b, :, slot].cpu().numpy(), s.beta[b])
 

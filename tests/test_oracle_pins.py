@@ -124,3 +124,36 @@ def test_exact_model_matches_oracle_on_floats():
                           g[:, None], None if beta is None else beta[:, None], S0[None])
         Sx = np.array([[float(x) for x in r] for r in S_x])
         assert np.abs(S[0] - Sx).max() <= 1e-12 * max(1, np.abs(Sx).max())
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("n", [1, 2, 3, 6])
+def test_wy_readout_equals_chain_readout(variant, n):
+    """The compact-WY readout (R = (I + N)^{-1}, no sequential chain) equals the
+    q-chain readout and the eager state's readout, exactly."""
+    rng = np.random.default_rng(300 + 10 * variant + n)
+    d = 4
+    S0, qs, ks, vs, alphas, betas = _exact_case(variant, rng, n, d)
+    log = [(ks[j], vs[j], alphas[j], None if betas is None else betas[j]) for j in range(n)]
+    q = qs[-1]
+    o_wy = exact.wy_readout(variant, S0, log, q)
+    assert o_wy == exact.qchain_readout(variant, S0, log, q)
+    _, S_e = exact.run_stepwise(variant, S0, qs, ks, vs, alphas, betas)
+    assert o_wy == exact.matvec(S_e, q)
+
+
+@pytest.mark.parametrize("variant", [GDN, KDA])
+def test_wy_r_is_inverse_of_unit_triangular(variant):
+    """R built one column per appended entry is (I + N)^{-1}."""
+    rng = np.random.default_rng(400 + variant)
+    n, d = 5, 3
+    _, _, ks, vs, alphas, betas = _exact_case(variant, rng, n, d)
+    log = [(ks[j], vs[j], alphas[j], betas[j]) for j in range(n)]
+    R = exact.wy_build_r(variant, log)
+    Nm = [[Fr(0)] * n for _ in range(n)]
+    for j in range(1, n):
+        u = exact.wy_t_column(variant, log, j)
+        for i in range(j):
+            Nm[i][j] = u[i]
+    I_plus_N = exact.madd(exact.eye(n), Nm)
+    assert exact.matmul(I_plus_N, R) == exact.eye(n)

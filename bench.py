@@ -53,7 +53,8 @@ def byte_model(wl: W.Workload):
     In = (2 * dk + dv) * es + g + b                    # q, k, v, g, beta
     Out = 4 * dv                                       # fp32 o
     E = (dk + dv) * es + g + b                         # one log entry
-    return dict(St=St, In=In, Out=Out, E=E)
+    R = 1 if wl.has_beta else 0                        # delta rule: packed R columns
+    return dict(St=St, In=In, Out=Out, E=E, R=R)
 
 
 def eager_bytes(m):
@@ -63,8 +64,11 @@ def eager_bytes(m):
 
 def log_step_bytes(m, c_prev):
     """Per state with c_prev logged entries: read S0 and the logged entries,
-    read inputs, append one entry, write o, read and write the fill counter."""
-    return m["St"] + c_prev * m["E"] + m["In"] + m["E"] + m["Out"] + 8
+    read inputs, append one entry, write o, read and write the fill counter;
+    delta-rule variants also read the c_prev (c_prev - 1) / 2 stored
+    key-side factors and write the new entry's c_prev."""
+    r = m["R"] * 4 * (c_prev * (c_prev - 1) // 2 + c_prev)
+    return m["St"] + c_prev * m["E"] + m["In"] + m["E"] + m["Out"] + 8 + r
 
 
 def merge_bytes(m, n):

@@ -13,15 +13,11 @@
 // written exactly once per step.
 //
 // The DeltaLog step leaves the base S0 untouched (Core Mechanism: appends of
-// compact factors instead of dense write-back).  Its readout pulls q back
-// through the logged transforms, newest first -- the key-side work the
-// page's Kernel Implementation stages once per slot and head ("ReplayPrep")
-// and shares with the value-side work ("AppendDecode"):
-//   coef_j = beta_j k_j.q_j (additive: k_j.q_j),
-//   q_{j-1} = alpha_j (q_j - coef_j k_j) (additive: w_j q_j),
-//   o = S0 q_0 + sum_j coef_j v_j.
-// Wave 0 runs that chain while the other waves' S0 loads are in flight and
-// they append the new entry; all four waves then read out their value rows.
+// compact factors instead of dense write-back) and reads out S0 q0 plus a
+// combination of the logged values, with q0 and the coefficients formed by
+// the key side in compact WY form (see the log step kernel below).  Four
+// waves per (row, head) hold S0 in registers while they share that key-side
+// work through LDS.
 #include "dl_common.hpp"
 
 namespace dl {

@@ -32,6 +32,7 @@ struct Params {
     float *log_t;      // packed columns of the compact-WY factor R (delta-rule variants)
     int *fill;
     int *flags;
+    int stream;        // 1: state loads and stores carry the nontemporal hint
 };
 
 template <int D>
@@ -46,6 +47,30 @@ struct Shape {
 };
 
 __device__ __forceinline__ int col_of(int s, int m, int e) { return 4 * s + 32 * m + e; }
+// State tiles.  When a call's states are larger than the last-level cache
+// can usefully hold (NT), every state is read (and written) once per kernel
+// with the nontemporal hint: the lines do not displace reusable data and the
+// streaming read rate rises measurably on gfx950.  Smaller state sets keep
+// ordinary cacheable accesses, so repeated calls can hit the cache.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <bool NT>
+__device__ __forceinline__ float4 load_state4(const float *p) {
+    if constexpr (NT) {
+        const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+        return make_float4(t.x, t.y, t.z, t.w);
+    } else {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+}
+template <bool NT>
+__device__ __forceinline__ void store_state4(float *p, float4 v) {
+    if constexpr (NT) {
+        const f32x4 t = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(p));
+    } else {
+        *reinterpret_cast<float4 *>(p) = v;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // input element access: fp32 or bf16 (stored as uint16 bit patterns)

@@ -59,7 +59,7 @@ __device__ __forceinline__ bool resolve_merge_pair(const Params &P, const int *s
 // ---------------------------------------------------------------------------
 // replay merge (VALU)
 // ---------------------------------------------------------------------------
-template <int V, int D, typename T>
+template <int V, int D, typename T, bool NT>
 __global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *__restrict__ slot_idx,
                                                            int mode) {
     using SH = Shape<D>;
@@ -80,7 +80,7 @@ __global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *
         const int row = wave * SH::RPW + it * 8 + grp;
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m)
-            st[it][m] = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + col_of(s, m, 0));
+            st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
     const unsigned char *sk = smem + lp.off_k;
     const float *sa = reinterpret_cast<const float *>(smem + lp.off_a);
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *
         const int row = wave * SH::RPW + it * 8 + grp;
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m)
-            *reinterpret_cast<float4 *>(Sp + (size_t)row * D + col_of(s, m, 0)) = st[it][m];
+            store_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0), st[it][m]);
     }
     if (tid == 0)
         P.fill[pair] = 0;
@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *
 // contractions on its rows.  The value loads of the chunk are issued before
 // the key-side phases so they overlap them.
 // ---------------------------------------------------------------------------
-template <int V, int D, typename T>
+template <int V, int D, typename T, bool NT>
 __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__restrict__ slot_idx,
                                                        int mode) {
     constexpr int C = 16;               // entries per WY chunk
@@ -189,7 +189,7 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
         const int row = 16 * (wave * NIT + it) + li;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const float4 x = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + 4 * kg + 16 * m);
+            const float4 x = load_state4<NT>(Sp + (size_t)row * D + 4 * kg + 16 * m);
             st[it][m] = floatx4{x.x, x.y, x.z, x.w};
         }
     }
@@ -355,8 +355,8 @@ __global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__re
         const int row = 16 * (wave * NIT + it) + li;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
-            *reinterpret_cast<float4 *>(Sp + (size_t)row * D + 4 * kg + 16 * m) =
-                make_float4(st[it][m][0], st[it][m][1], st[it][m][2], st[it][m][3]);
+            store_state4<NT>(Sp + (size_t)row * D + 4 * kg + 16 * m,
+                          make_float4(st[it][m][0], st[it][m][1], st[it][m][2], st[it][m][3]));
     }
     if (tid == 0)
         P.fill[pair] = 0;
@@ -391,16 +391,24 @@ static hipError_t replay_t(const Params &P, int rows, const int *slot_idx, int m
                            const Launch &ln) {
     const int CH = P.L < 32 ? P.L : 32;
     const LdsPlan lp = lds_plan(V, D, (int)sizeof(T), CH, P.L, true);
-    hipExtLaunchKernelGGL((merge_replay_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), lp.bytes,
-                       ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode);
+    if (P.stream)
+        hipExtLaunchKernelGGL((merge_replay_kernel<V, D, T, true>), dim3(rows * P.heads), dim3(256), lp.bytes,
+                              ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode);
+    else
+        hipExtLaunchKernelGGL((merge_replay_kernel<V, D, T, false>), dim3(rows * P.heads), dim3(256), lp.bytes,
+                              ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode);
     return hipGetLastError();
 }
 
 template <int V, int D, typename T>
 static hipError_t wy_t(const Params &P, int rows, const int *slot_idx, int mode,
                        const Launch &ln) {
-    hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start, ln.stop, 0, P,
-                       slot_idx, mode);
+    if (P.stream)
+        hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T, true>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start,
+                              ln.stop, 0, P, slot_idx, mode);
+    else
+        hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T, false>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start,
+                              ln.stop, 0, P, slot_idx, mode);
     return hipGetLastError();
 }
 

@@ -44,7 +44,7 @@ hipError_t launch_zero(void *p, size_t bytes, const Launch &ln) {
 // ---------------------------------------------------------------------------
 // eager step
 // ---------------------------------------------------------------------------
-template <int V, int D, typename T>
+template <int V, int D, typename T, bool NT>
 __global__ void __launch_bounds__(256)
 eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                   const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
@@ -74,7 +74,7 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
         const int row = wave * SH::RPW + it * 8 + grp;
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m)
-            st[it][m] = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + col_of(s, m, 0));
+            st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
     float kc[SH::FPL], qc[SH::FPL], ac[SH::FPL];
 #pragma unroll
@@ -144,8 +144,7 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
                 const float decayed = (V == GDN) ? alpha * sv[e] : sv[e] * ac[f];
                 sv[e] = decayed + d * kc[f];
             }
-            *reinterpret_cast<float4 *>(Sp + (size_t)row * D + col_of(s, m, 0)) =
-                make_float4(sv[0], sv[1], sv[2], sv[3]);
+            store_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0), make_float4(sv[0], sv[1], sv[2], sv[3]));
         }
         if (s == 0)
             orow[row] = p + d * kq;
@@ -214,7 +213,7 @@ __device__ __forceinline__ void stage_log(const Params &P, size_t pair, int n, u
     }
 }
 
-template <int V, int D, typename T, bool APPEND, int MV>
+template <int V, int D, typename T, bool APPEND, int MV, bool NT>
 __global__ void __launch_bounds__(256)
 log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                 const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
@@ -261,7 +260,7 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
         const int row = wave * SH::RPW + it * 8 + grp;
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m)
-            st[it][m] = *reinterpret_cast<const float4 *>(Sp + (size_t)row * D + col_of(s, m, 0));
+            st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
     const int cg = lane % G, ro = lane / G, ch0 = 8 * cg;
     float qv[8], kn[8];
@@ -587,32 +586,44 @@ template <int V, int D, typename T>
 static hipError_t eager_t(const Params &P, int rows, const int *slot_idx, const void *q,
                           const void *k, const void *v, const float *g, const float *beta,
                           float *o, const Launch &ln) {
-    hipExtLaunchKernelGGL((eager_step_kernel<V, D, T>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start, ln.stop, 0,
-                       P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
-                       static_cast<const T *>(v), g, beta, o);
+    if (P.stream)
+        hipExtLaunchKernelGGL((eager_step_kernel<V, D, T, true>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start,
+                              ln.stop, 0, P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
+                              static_cast<const T *>(v), g, beta, o);
+    else
+        hipExtLaunchKernelGGL((eager_step_kernel<V, D, T, false>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start,
+                              ln.stop, 0, P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
+                              static_cast<const T *>(v), g, beta, o);
     return hipGetLastError();
+}
+
+template <int V, int D, typename T, bool APPEND, int MV>
+static void log_launch(const Params &P, int rows, const int *slot_idx, const void *q,
+                       const void *k, const void *v, const float *g, const float *beta,
+                       float *o, const Launch &ln) {
+    const StepPlan sp = step_plan(V, D, (int)sizeof(T), P.L);
+    const dim3 grid(rows * P.heads), block(256);
+    if (P.stream)
+        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, MV, true>), grid, block, sp.bytes, ln.stream, ln.start,
+                              ln.stop, 0, P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
+                              static_cast<const T *>(v), g, beta, o);
+    else
+        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, MV, false>), grid, block, sp.bytes, ln.stream, ln.start,
+                              ln.stop, 0, P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
+                              static_cast<const T *>(v), g, beta, o);
 }
 
 template <int V, int D, typename T, bool APPEND>
 static hipError_t log_t(const Params &P, int rows, const int *slot_idx, const void *q,
                         const void *k, const void *v, const float *g, const float *beta,
                         float *o, const Launch &ln) {
-    const StepPlan sp = step_plan(V, D, (int)sizeof(T), P.L);
-    const dim3 grid(rows * P.heads), block(256);
     // MV = value-log entries per lane per row = ceil(L / 8), rounded up to 2, 4 or 8
-    if (P.L <= 16) {
-        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 2>), grid, block, sp.bytes, ln.stream, ln.start, ln.stop, 0,
-                           P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
-                           static_cast<const T *>(v), g, beta, o);
-    } else if (P.L <= 32) {
-        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 4>), grid, block, sp.bytes, ln.stream, ln.start, ln.stop, 0,
-                           P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
-                           static_cast<const T *>(v), g, beta, o);
-    } else {
-        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, 8>), grid, block, sp.bytes, ln.stream, ln.start, ln.stop, 0,
-                           P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
-                           static_cast<const T *>(v), g, beta, o);
-    }
+    if (P.L <= 16)
+        log_launch<V, D, T, APPEND, 2>(P, rows, slot_idx, q, k, v, g, beta, o, ln);
+    else if (P.L <= 32)
+        log_launch<V, D, T, APPEND, 4>(P, rows, slot_idx, q, k, v, g, beta, o, ln);
+    else
+        log_launch<V, D, T, APPEND, 8>(P, rows, slot_idx, q, k, v, g, beta, o, ln);
     return hipGetLastError();
 }
 

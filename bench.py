@@ -122,7 +122,9 @@ def parse_args(argv=None):
     ap.add_argument("--config", type=int, default=2, choices=sorted(W.WORKLOADS))
     ap.add_argument("--L", type=int, default=None, help="log slots (default: the workload's)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--paths", default="eager,log")
+    ap.add_argument("--paths", default="eager,log,log-fused",
+                    help="eager; log (merge launched after the step that fills a log); "
+                         "log-fused (that step merges in the same pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
@@ -257,7 +259,8 @@ def main(argv=None):
     for path in paths:
         states = []
         for l in range(layers):
-            st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype, device=dev)
+            st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype, device=dev,
+                               merge_on_step=(path == "log-fused"))
             st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
             states.append(st)
         O = torch.zeros((T, U, H, d), dtype=torch.float32, device=dev)
@@ -291,7 +294,7 @@ def main(argv=None):
                 if path != "eager":
                     if l == 0:
                         fills[act[tau]] += 1
-                    if wl.ragged or np.any(fills == L):
+                    if path == "log" and (wl.ragged or np.any(fills == L)):
                         plan.append((tau, "merge", st.handle, (Bt, None, B.DL_MERGE_FULL, stream)))
                     if l == layers - 1:
                         fills[fills == L] = 0
@@ -350,11 +353,16 @@ def main(argv=None):
             f = fills_at_start.copy()
             for tau in range(prefix + Wu, T):
                 for l in range(layers):
-                    step_bytes.append(float(np.sum([log_step_bytes(m, c) for c in f])) * H)
+                    if path == "log-fused":
+                        # the step that fills a log also writes the merged base
+                        step_bytes.append(float(np.sum([log_step_bytes(m, c) + (m["St"] if c == L - 1 else 0)
+                                                        for c in f])) * H)
+                    else:
+                        step_bytes.append(float(np.sum([log_step_bytes(m, c) for c in f])) * H)
                     if l == layers - 1:
                         f += 1
                         full = f == L
-                        if wl.ragged or full.any():     # a merge launch ran after this step
+                        if path == "log" and (wl.ragged or full.any()):   # a merge launch followed
                             mbytes += layers * H * (merge_bytes(m, L) * full.sum() + 4 * (~full).sum())
                             mflops += layers * H * merge_flops(wl, L) * full.sum()
                         f[full] = 0
@@ -402,11 +410,13 @@ def main(argv=None):
                      "batch": Bt, "layers": layers, "heads": H, "d_k": d, "d_v": wl.d_v,
                      "log_len": L, "input_dtype": wl.dtype, "state_dtype": "fp32",
                      "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix}
-    main_path = "log" if "log" in results else paths[0]
+    main_path = next((p for p in ("log-fused", "log") if p in results), paths[0])
     r = results[main_path]
     out["value"] = r["updates_per_s"]
     out["ms_per_step"] = r["ms_per_step"]
-    kname = "log_step_kernel" if main_path == "log" else "eager_step_kernel"
+    out["path"] = main_path
+    kname = {"log-fused": "log_step_kernel.fused", "log": "log_step_kernel"}.get(main_path,
+                                                                                 "eager_step_kernel")
     out["roofline"] = {"bound": "hbm", "kernel": kname,
                        "achieved": r["step_kernel_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": r["step_kernel_GBps"] / HBM_PEAK_GBPS,
@@ -422,13 +432,21 @@ def main(argv=None):
                         "algorithmic_bytes_per_launch": e["step_bytes_per_launch"],
                         "traffic": counter_traffic("eager_step_kernel", wl.name)}
         out["speedup_vs_eager"] = r["updates_per_s"] / e["updates_per_s"]
-    if main_path == "log" and r["merge_launches"]:
-        ms = r["merge_ms_total"] / 1e3
-        out["merge"] = {"kernel": "merge_wy_kernel", "launches": r["merge_launches"],
-                        "share_of_step_time": r["merge_ms_total"] / r["total_ms"],
-                        "GBps": r["merge_bytes"] / ms / 1e9 if ms else None,
-                        "mfma_TFLOPs": r["merge_flops"] / ms / 1e12 if ms else None,
-                        "mfma_frac": (r["merge_flops"] / ms / 1e12 / FP32_MFMA_PEAK_TFLOPS) if ms else None}
+    if main_path != "log" and "log" in results:
+        u = results["log"]
+        out["log_separate_merge"] = {"value": u["updates_per_s"], "ms_per_step": u["ms_per_step"],
+                                     "kernel": "log_step_kernel", "achieved_GBps": u["step_kernel_GBps"],
+                                     "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS,
+                                     "avg_launch_us": u["step_kernel_avg_us"],
+                                     "traffic": counter_traffic("log_step_kernel", wl.name)}
+    if "log" in results and results["log"]["merge_launches"]:
+        u = results["log"]
+        ms = u["merge_ms_total"] / 1e3
+        out["merge"] = {"kernel": "merge_wy_kernel", "launches": u["merge_launches"],
+                        "share_of_step_time": u["merge_ms_total"] / u["total_ms"],
+                        "GBps": u["merge_bytes"] / ms / 1e9 if ms else None,
+                        "mfma_TFLOPs": u["merge_flops"] / ms / 1e12 if ms else None,
+                        "mfma_frac": (u["merge_flops"] / ms / 1e12 / FP32_MFMA_PEAK_TFLOPS) if ms else None}
 
     # ---- the oracle on the host cores, same inputs, sampled states
     if not args.no_cpu_baseline:

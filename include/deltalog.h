@@ -87,6 +87,9 @@ typedef struct {
     int32_t d_v;       /* value channels: must equal d_k */
     int32_t log_len;   /* L, log slots per (unit, head): 0 (eager only) .. 64 */
     int32_t in_dtype;  /* dl_dtype of q, k, v and of the logged k, v copies */
+    int32_t merge_on_step; /* 0: a full log waits for dl_merge; 1: the log step
+                            * that fills a log also merges it into the base in
+                            * the same pass and leaves fill at 0 */
 } dl_desc;
 
 /* Device pointers into a state block (all row-major, contiguous).

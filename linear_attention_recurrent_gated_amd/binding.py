@@ -28,7 +28,8 @@ DL_FLAG_LOG_FULL, DL_FLAG_LOG_NONEMPTY, DL_FLAG_BAD_SLOT = 1, 2, 4
 class DlDesc(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("units", ctypes.c_int32),
                 ("heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
-                ("log_len", ctypes.c_int32), ("in_dtype", ctypes.c_int32)]
+                ("log_len", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("merge_on_step", ctypes.c_int32)]
 
 
 class DlStatePtrs(ctypes.Structure):
@@ -171,15 +172,16 @@ class DecodeState:
     """
 
     def __init__(self, variant: int, units: int, heads: int, d: int, log_len: int,
-                 dtype: str = "bf16", device="cuda", stream=None):
+                 dtype: str = "bf16", device="cuda", stream=None, merge_on_step: bool = False):
         import torch
 
         self.torch = torch
         self.variant, self.units, self.heads, self.d, self.L = variant, units, heads, d, log_len
         self.dtype = dtype
         self.in_torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
+        self.merge_on_step = bool(merge_on_step)
         self.desc = DlDesc(variant, units, heads, d, d, log_len,
-                           DL_BF16 if dtype == "bf16" else DL_F32)
+                           DL_BF16 if dtype == "bf16" else DL_F32, int(self.merge_on_step))
         nbytes = dl_state_bytes(self.desc)
         if nbytes == 0:
             raise DlError(DL_ERR_INVALID, dl_last_error())

@@ -52,6 +52,8 @@ dl_status check_desc(const dl_desc *d) {
         return fail(DL_ERR_INVALID, "unknown input dtype %d", d->in_dtype);
     if (d->log_len < 0)
         return fail(DL_ERR_INVALID, "log_len must be >= 0, got %d", d->log_len);
+    if (d->merge_on_step != 0 && d->merge_on_step != 1)
+        return fail(DL_ERR_INVALID, "merge_on_step must be 0 or 1, got %d", d->merge_on_step);
     if (d->d_k != d->d_v)
         return fail(DL_ERR_UNSUPPORTED, "d_k (%d) != d_v (%d) is not built", d->d_k, d->d_v);
     if (d->d_k != 64 && d->d_k != 128)
@@ -134,7 +136,8 @@ dl_status check_step_args(const dl_state *st, int32_t rows, const int32_t *slot_
 // device's per-workgroup LDS (160 KiB on gfx950).
 dl_status check_lds(const dl_state *st) {
     const int es = st->desc.in_dtype == DL_BF16 ? 2 : 4;
-    const dl::StepPlan lp = dl::step_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len);
+    const dl::StepPlan lp = dl::step_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len,
+                                          st->desc.merge_on_step != 0);
     if (lp.bytes <= 65536)
         return DL_OK;
     int dev = 0, max_lds = 0;
@@ -202,6 +205,7 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.L = desc->log_len;
     p.dtype = desc->in_dtype;
     p.flags = reinterpret_cast<int *>(m + l.off_flags);
+    p.fuse = desc->merge_on_step;
     // stream the state when the base is more than half of MI355X's 256 MiB
     // Infinity Cache: such a state set cannot stay resident between calls
     p.stream = (size_t)desc->units * desc->heads * desc->d_v * desc->d_k * 4 > ((size_t)128 << 20);

@@ -33,6 +33,7 @@ struct Params {
     int *fill;
     int *flags;
     int stream;        // 1: state loads and stores carry the nontemporal hint
+    int fuse;          // 1: the log step that fills a log merges it
 };
 
 template <int D>
@@ -185,12 +186,15 @@ struct KeyLayout {
 // of one wave's direct-to-LDS load (64 lanes x 16 or 4 bytes).
 struct StepPlan {
     int off_k;     // staged keys, rows of D elements in the input dtype
+    int off_v;     // staged values, rows of D elements in the input dtype
     int off_lam;   // staged cumulative log-decays, rows of D floats (per-key decays)
     int off_t;     // staged columns of R, packed
     int off_r, off_u, off_f, off_l;   // per-entry scalars, 64 floats each
+    int off_bn;    // beta of the appended entry
     int off_c, off_e;                 // per-wave coefficients, 4 x 64 floats each
     int off_qin;   // q as floats, D
     int off_q;     // q0, D floats
+    int off_y;     // merge in the step: 16 rows of Y = R Q, D floats each
     int bytes;
 };
 
@@ -200,20 +204,23 @@ __host__ __device__ inline int packed_t_len(int variant, int L) {
 
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-__host__ __device__ inline StepPlan step_plan(int variant, int D, int esize, int L) {
+__host__ __device__ inline StepPlan step_plan(int variant, int D, int esize, int L, bool fuse) {
     StepPlan p;
     p.off_k = 0;
-    p.off_lam = round_up(L * D * esize, 1024);
+    p.off_v = round_up(L * D * esize, 1024);
+    p.off_lam = p.off_v + round_up(L * D * esize, 1024);
     p.off_t = p.off_lam + (variant == DL_GDN ? 0 : round_up(L * D * 4, 1024));
     p.off_r = p.off_t + round_up(packed_t_len(variant, L) * 4, 256);
     p.off_u = p.off_r + 256;
     p.off_f = p.off_u + 256;
     p.off_l = p.off_f + 256;
-    p.off_c = p.off_l + 256;
+    p.off_bn = p.off_l + 256;
+    p.off_c = p.off_bn + 16;
     p.off_e = p.off_c + 4 * 256;
     p.off_qin = p.off_e + 4 * 256;
     p.off_q = p.off_qin + D * 4;
-    p.bytes = p.off_q + D * 4;
+    p.off_y = p.off_q + D * 4;
+    p.bytes = p.off_y + (fuse ? 16 * D * 4 : 0);
     return p;
 }
 

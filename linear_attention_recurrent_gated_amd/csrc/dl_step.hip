@@ -178,8 +178,8 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
 // ---------------------------------------------------------------------------
 
 // This wave's share of the staging of entries [0, n) of `pair` into LDS
-// (direct-to-LDS loads, every fourth batch of 64 lanes): keys, cumulative
-// log-decays (per-key decays) and the packed R columns.  Lanes past the last
+// (direct-to-LDS loads, every fourth batch of 64 lanes): keys, values,
+// cumulative log-decays (per-key decays) and the packed R columns.  Lanes past the last
 // element are masked off, so nothing is written past entry n - 1.
 template <int V, int D, typename T>
 __device__ __forceinline__ void stage_log(const Params &P, size_t pair, int n, unsigned char *smem,
@@ -188,10 +188,13 @@ __device__ __forceinline__ void stage_log(const Params &P, size_t pair, int n, u
     constexpr int CPR = D * (int)sizeof(T) / 16;
     const int nk = n * CPR;
     const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_k) + e0 * D);
+    const uint4 *vs = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_v) + e0 * D);
     for (int b = 64 * wave; b < nk; b += 256) {
         const int idx = b + lane;
-        if (idx < nk)
+        if (idx < nk) {
             load_to_lds<16>(ks + idx, smem + sp.off_k + 16 * b);
+            load_to_lds<16>(vs + idx, smem + sp.off_v + 16 * b);
+        }
     }
     if constexpr (V != GDN) {
         const int nl = n * (D / 4);
@@ -213,8 +216,204 @@ __device__ __forceinline__ void stage_log(const Params &P, size_t pair, int n, u
     }
 }
 
-template <int V, int D, typename T, bool APPEND, int MV, bool NT>
-__global__ void __launch_bounds__(256)
+// Merge in the step that fills the log (all ct = L entries staged, R
+// complete in LDS, this wave's rows of S0 in registers):
+//   S' = S0 diag(E_c) + (V^T - S0 Kt^T) Y,   Kt_j = E_j k_j,   Y = R Q,
+//   Q_i = beta_i k_i D(i, c)   (additive variant: R = I, beta = 1),
+// the readout formula written for every q at once.  Z = V^T - S0 Kt^T is
+// formed first, while S0 is intact, and kept in registers (lane s of a row
+// group holds the entries j = s + 8 mm); then S0 diag(E_c) + Z Y, with Y
+// built 16 rows at a time by all waves, becomes the new base; fill = 0.
+template <int V, int D, typename T, int MV, bool NT>
+__device__ __forceinline__ void merge_in_step(const Params &P, size_t pair, int ct, unsigned char *smem,
+                                              const StepPlan &sp,
+                                              float4 (&st)[Shape<D>::ITER][Shape<D>::NCH],
+                                              const float (&vc)[Shape<D>::ITER], float lam_c) {
+    using SH = Shape<D>;
+    constexpr int ITER = SH::ITER, NCH = SH::NCH;
+    const int n = ct - 1;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int grp = lane >> 3, s = lane & 7;
+    const float *slam = reinterpret_cast<const float *>(smem + sp.off_lam);
+    const float *sT = reinterpret_cast<const float *>(smem + sp.off_t);
+    const float *sf = reinterpret_cast<const float *>(smem + sp.off_f);
+    const float *sl = reinterpret_cast<const float *>(smem + sp.off_l);
+    const T *vr = reinterpret_cast<const T *>(smem + sp.off_v);
+    float *sy = reinterpret_cast<float *>(smem + sp.off_y);
+    const unsigned char *kbase = smem + sp.off_k;
+    auto krow = [&](int j) { return kbase + (size_t)j * D * sizeof(T); };
+
+    // ---- Z[row][j] = v_j[row] - S0[row, :] . (E_j k_j), one entry at a time
+    float zr[ITER][MV];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it)
+#pragma unroll
+        for (int mm = 0; mm < MV; ++mm)
+            zr[it][mm] = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < MV; ++mm) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = 8 * mm + u;
+            if (j >= ct)
+                break;
+            float w[ITER];
+#pragma unroll
+            for (int it = 0; it < ITER; ++it)
+                w[it] = 0.f;
+            if constexpr (V != RWKV6) {
+#pragma unroll
+                for (int m = 0; m < NCH; ++m) {
+                    float4 kt = lds_load4<T>(krow(j), col_of(s, m, 0));
+                    if constexpr (V == GDN) {
+                        const float e = fast_exp(sl[j]);
+                        kt.x *= e, kt.y *= e, kt.z *= e, kt.w *= e;
+                    } else {
+                        const float4 l4 = *reinterpret_cast<const float4 *>(slam + j * D + col_of(s, m, 0));
+                        kt.x *= fast_exp(l4.x), kt.y *= fast_exp(l4.y);
+                        kt.z *= fast_exp(l4.z), kt.w *= fast_exp(l4.w);
+                    }
+#pragma unroll
+                    for (int it = 0; it < ITER; ++it)
+                        w[it] += st[it][m].x * kt.x + st[it][m].y * kt.y + st[it][m].z * kt.z + st[it][m].w * kt.w;
+                }
+            }
+#pragma unroll
+            for (int it = 0; it < ITER; ++it) {
+                const int row = wave * SH::RPW + it * 8 + grp;
+                const float wsum = (V == RWKV6) ? 0.f : sum8(w[it]);
+                const float vj = (j < n) ? Elem<T>::load1(vr + j * D + row) : vc[it];
+                zr[it][mm] = (s == u) ? vj - wsum : zr[it][mm];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // ---- S' = S0 diag(E_c) + Z Y
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) {
+        if constexpr (V == GDN) {
+            const float e = fast_exp(lam_c);
+#pragma unroll
+            for (int it = 0; it < ITER; ++it)
+                st[it][m].x *= e, st[it][m].y *= e, st[it][m].z *= e, st[it][m].w *= e;
+        } else {
+            const float4 l4 = *reinterpret_cast<const float4 *>(slam + n * D + col_of(s, m, 0));
+            const float4 e = make_float4(fast_exp(l4.x), fast_exp(l4.y), fast_exp(l4.z), fast_exp(l4.w));
+#pragma unroll
+            for (int it = 0; it < ITER; ++it)
+                st[it][m].x *= e.x, st[it][m].y *= e.y, st[it][m].z *= e.z, st[it][m].w *= e.w;
+        }
+    }
+    constexpr int TPC = 256 / D;          // threads per key channel building Y
+    constexpr int JPT = 16 / TPC;         // rows of the Y chunk per thread
+    const int ych = tid % D, ysub = tid / D;
+    const float lc_y = (V == GDN) ? 0.f : slam[n * D + ych];
+    const int gbase = lane & ~7;
+#pragma unroll
+    for (int c = 0; c < MV / 2; ++c) {
+        const int j0 = 16 * c;
+        if (j0 >= ct)
+            break;
+        __syncthreads();   // the previous chunk of Y is consumed
+        {
+            // Y_j[ch] = sum_{i >= j} R[j, i] Q_i[ch] for j = jb .. jb + JPT - 1
+            const int jb = j0 + JPT * ysub;
+            float acc[JPT];
+#pragma unroll
+            for (int u = 0; u < JPT; ++u)
+                acc[u] = 0.f;
+            for (int i = jb; i < ct; ++i) {
+                float qi = sf[i] * Elem<T>::load1(reinterpret_cast<const T *>(krow(i)) + ych);
+                if constexpr (V != GDN)
+                    qi *= fast_exp(lc_y - slam[i * D + ych]);
+#pragma unroll
+                for (int u = 0; u < JPT; ++u) {
+                    const int j = jb + u;
+                    float r = (j == i) ? 1.f : 0.f;
+                    if constexpr (V != RWKV6)
+                        r = (j < i) ? sT[i * (i - 1) / 2 + j] : r;
+                    acc[u] += r * qi;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < JPT; ++u)
+                sy[(JPT * ysub + u) * D + ych] = acc[u];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int mm = 2 * c + h;
+            for (int u = 0; u < 8; ++u) {
+                const int j = 8 * mm + u;
+                if (j >= ct)
+                    break;
+                float4 y[NCH];
+#pragma unroll
+                for (int m = 0; m < NCH; ++m)
+                    y[m] = *reinterpret_cast<const float4 *>(sy + (j - j0) * D + col_of(s, m, 0));
+#pragma unroll
+                for (int it = 0; it < ITER; ++it) {
+                    const float z = __shfl(zr[it][mm], gbase | u);
+#pragma unroll
+                    for (int m = 0; m < NCH; ++m) {
+                        st[it][m].x += z * y[m].x, st[it][m].y += z * y[m].y;
+                        st[it][m].z += z * y[m].z, st[it][m].w += z * y[m].w;
+                    }
+                }
+            }
+        }
+    }
+
+    float *Sp = P.base + pair * D * D;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+        const int row = wave * SH::RPW + it * 8 + grp;
+#pragma unroll
+        for (int m = 0; m < NCH; ++m)
+            store_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0), st[it][m]);
+    }
+    if (tid == 0)
+        P.fill[pair] = 0;
+}
+
+// Entry n of the log, from its LDS copies to HBM (wave 0, after the last
+// barrier): k and v (bit copies of the inputs), the decay accumulated through
+// it, beta, and column n of R.
+template <int V, int D, typename T>
+__device__ __forceinline__ void log_append(const Params &P, size_t pair, int n, const unsigned char *smem,
+                                           const StepPlan &sp, int lane) {
+    const size_t e = pair * P.L + n;
+    constexpr int CPR = D * (int)sizeof(T) / 16;     // 16-byte chunks per row
+    if (lane < CPR) {
+        const uint4 *kr = reinterpret_cast<const uint4 *>(smem + sp.off_k + (size_t)n * D * sizeof(T));
+        const uint4 *vr = reinterpret_cast<const uint4 *>(smem + sp.off_v + (size_t)n * D * sizeof(T));
+        reinterpret_cast<uint4 *>(static_cast<T *>(P.log_k) + e * D)[lane] = kr[lane];
+        reinterpret_cast<uint4 *>(static_cast<T *>(P.log_v) + e * D)[lane] = vr[lane];
+    }
+    if constexpr (V == GDN) {
+        if (lane == 0)
+            P.log_g[e] = reinterpret_cast<const float *>(smem + sp.off_l)[n];
+    } else {
+        if (lane < D / 4) {
+            const float4 *lr = reinterpret_cast<const float4 *>(smem + sp.off_lam + (size_t)n * D * 4);
+            reinterpret_cast<float4 *>(P.log_g + e * D)[lane] = lr[lane];
+        }
+    }
+    if constexpr (V != RWKV6) {
+        if (lane == 0)
+            P.log_beta[e] = *reinterpret_cast<const float *>(smem + sp.off_bn);
+        if (lane < n)
+            P.log_t[pair * packed_t_len(V, P.L) + n * (n - 1) / 2 + lane] =
+                reinterpret_cast<const float *>(smem + sp.off_t)[n * (n - 1) / 2 + lane];
+    }
+}
+
+// With the merge fused in (bf16 inputs, logs of up to 32 entries) the kernel
+// is held to four waves per SIMD, i.e. four workgroups per CU, like the
+// plain step.
+template <int V, int D, typename T, bool APPEND, int MV, bool NT, bool FUSE>
+__global__ void __launch_bounds__(256, (FUSE && MV <= 4 && sizeof(T) == 2) ? 4 : 1)
 log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                 const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
                 const float *__restrict__ beta, float *__restrict__ o) {
@@ -237,13 +436,14 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
     const size_t pair = (size_t)unit * H + h;
     const size_t io = (size_t)pr * D;
     const size_t e0 = pair * L;
-    const StepPlan sp = step_plan(V, D, (int)sizeof(T), L);
+    const StepPlan sp = step_plan(V, D, (int)sizeof(T), L, FUSE);
     float *slam = reinterpret_cast<float *>(smem + sp.off_lam);
-    const float *sT = reinterpret_cast<const float *>(smem + sp.off_t);
+    float *sT = reinterpret_cast<float *>(smem + sp.off_t);
     float *sr = reinterpret_cast<float *>(smem + sp.off_r);
     float *su = reinterpret_cast<float *>(smem + sp.off_u);
     float *sf = reinterpret_cast<float *>(smem + sp.off_f);
     float *sl = reinterpret_cast<float *>(smem + sp.off_l);
+    float *sb_new = reinterpret_cast<float *>(smem + sp.off_bn);
     float *sc = reinterpret_cast<float *>(smem + sp.off_c) + 64 * wave;
     float *se = reinterpret_cast<float *>(smem + sp.off_e) + 64 * wave;
     float *sq = reinterpret_cast<float *>(smem + sp.off_q);
@@ -253,6 +453,11 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
     // ---- loads that need nothing: fill, this wave's rows of S0, the inputs
     const int n = P.fill[pair];
     const int grp = lane >> 3, s = lane & 7;
+    // logged value v_j[row] (staged); 0 past the n stored entries
+    auto vlog = [&](int j, int row) {
+        const T *vr = reinterpret_cast<const T *>(smem + sp.off_v);
+        return j < n ? Elem<T>::load1(vr + (j < n ? j : 0) * D + row) : 0.f;
+    };
     const float *Sp = P.base + pair * D * D;
     float4 st[SH::ITER][SH::NCH];
 #pragma unroll
@@ -276,24 +481,10 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
     // ---- loads that need n: logged values of this wave's rows (clamped,
     //      branch-free; an empty log reads a dummy in-range address instead),
     //      the staging, and (wave 0) the per-entry scalars and the append
-    float vl[SH::ITER][MV];
-    float vc[SH::ITER];
-    {
-        const T *Vp = (n > 0) ? static_cast<const T *>(P.log_v) + e0 * D
-                              : reinterpret_cast<const T *>(P.base);
-        const int nl = n > 0 ? n - 1 : 0;
+    float vc[SH::ITER];       // the new entry's value on this lane's rows
 #pragma unroll
-        for (int it = 0; it < SH::ITER; ++it) {
-            const int row = wave * SH::RPW + it * 8 + grp;
-#pragma unroll
-            for (int mm = 0; mm < MV; ++mm) {
-                const int j = s + 8 * mm;
-                const float x = Elem<T>::load1(Vp + (size_t)(j < n ? j : nl) * D + row);
-                vl[it][mm] = (j < n) ? x : 0.f;
-            }
-            vc[it] = APPEND ? Elem<T>::load1(v + io + row) : 0.f;
-        }
-    }
+    for (int it = 0; it < SH::ITER; ++it)
+        vc[it] = APPEND ? Elem<T>::load1(v + io + wave * SH::RPW + it * 8 + grp) : 0.f;
     if (n > 0)
         stage_log<V, D, T>(P, pair, n, smem, sp, lane, wave);
     if (wave == 0) {
@@ -333,22 +524,16 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
                 lc[i] += gn[i];
         }
         if constexpr (APPEND) {
-            const size_t e = e0 + n;
+            // entry n goes to LDS now and to the log in HBM at the end of the
+            // kernel, so that no barrier waits for those stores
             if (ro == 0) {
-                store8<T>(static_cast<T *>(P.log_k) + e * D + ch0, kn);
-                store8<T>(static_cast<T *>(P.log_v) + e * D + ch0, vv);
                 store8<T>(krow(n) + ch0, kn);
-                if constexpr (V != GDN) {
-                    store8<float>(P.log_g + e * D + ch0, lc);
+                store8<T>(reinterpret_cast<T *>(smem + sp.off_v) + n * D + ch0, vv);
+                if constexpr (V != GDN)
                     store8<float>(slam + n * D + ch0, lc);
-                }
             }
-            if (lane == 0) {
-                if constexpr (V == GDN)
-                    P.log_g[e] = lam_c;
-                if constexpr (DELTA)
-                    P.log_beta[e] = b_in;
-            }
+            if (lane == 0)
+                sb_new[0] = b_in;
             if (lane == n) {
                 lam_j = lam_c;
                 b_j = b_in;
@@ -373,6 +558,7 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
 
     const int ct = APPEND ? n + 1 : n;   // entries the readout sees
     const int npass = (ct + PASS - 1) / PASS;
+
     float lam_c = 0.f, lc[8];
     if constexpr (V == GDN) {
         lam_c = ct > 0 ? sl[ct - 1] : 0.f;
@@ -458,7 +644,7 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
                 if (i < n) {
                     const float w = -acc_u;
                     if (wave == 0)
-                        P.log_t[pair * packed_t_len(V, L) + n * (n - 1) / 2 + i] = w;
+                        sT[n * (n - 1) / 2 + i] = w;   // logged at the end; read by a merge
                     coef += w * sr[n];
                 }
             }
@@ -545,15 +731,25 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
         }
 #pragma unroll
         for (int mm = 0; mm < MV; ++mm)
-            acc_o += cf[mm] * vl[it][mm];
+            acc_o += cf[mm] * vlog(s + 8 * mm, row);
         if (APPEND)
             acc_o += ccur * vc[it];
         acc_o = sum8(acc_o);
         if (s == 0)
             orow[row] = acc_o;
     }
-    if (APPEND && tid == 0)
-        P.fill[pair] = n + 1;
+    if constexpr (APPEND) {
+        if (wave == 0)
+            log_append<V, D, T>(P, pair, n, smem, sp, lane);
+        if constexpr (FUSE) {
+            if (n == L - 1) {
+                merge_in_step<V, D, T, MV, NT>(P, pair, ct, smem, sp, st, vc, lam_c);
+                return;
+            }
+        }
+        if (tid == 0)
+            P.fill[pair] = n + 1;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -601,16 +797,23 @@ template <int V, int D, typename T, bool APPEND, int MV>
 static void log_launch(const Params &P, int rows, const int *slot_idx, const void *q,
                        const void *k, const void *v, const float *g, const float *beta,
                        float *o, const Launch &ln) {
-    const StepPlan sp = step_plan(V, D, (int)sizeof(T), P.L);
+    const bool fuse = APPEND && P.fuse;
+    const StepPlan sp = step_plan(V, D, (int)sizeof(T), P.L, fuse);
     const dim3 grid(rows * P.heads), block(256);
-    if (P.stream)
-        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, MV, true>), grid, block, sp.bytes, ln.stream, ln.start,
-                              ln.stop, 0, P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
-                              static_cast<const T *>(v), g, beta, o);
-    else
-        hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, MV, false>), grid, block, sp.bytes, ln.stream, ln.start,
-                              ln.stop, 0, P, slot_idx, static_cast<const T *>(q), static_cast<const T *>(k),
-                              static_cast<const T *>(v), g, beta, o);
+#define DL_LOG_LAUNCH(NTV, FV)                                                                         \
+    hipExtLaunchKernelGGL((log_step_kernel<V, D, T, APPEND, MV, NTV, FV>), grid, block, sp.bytes,      \
+                          ln.stream, ln.start, ln.stop, 0, P, slot_idx, static_cast<const T *>(q),     \
+                          static_cast<const T *>(k), static_cast<const T *>(v), g, beta, o)
+    if constexpr (APPEND) {
+        if (P.stream) {
+            if (fuse) DL_LOG_LAUNCH(true, true); else DL_LOG_LAUNCH(true, false);
+        } else {
+            if (fuse) DL_LOG_LAUNCH(false, true); else DL_LOG_LAUNCH(false, false);
+        }
+    } else {
+        if (P.stream) DL_LOG_LAUNCH(true, false); else DL_LOG_LAUNCH(false, false);
+    }
+#undef DL_LOG_LAUNCH
 }
 
 template <int V, int D, typename T, bool APPEND>

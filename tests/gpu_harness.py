@@ -42,7 +42,10 @@ class Case:
 def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
              steps: int | None = None, pairs=None, merge_every_step: bool | None = None,
              run_oracle: bool = True, threads: int | None = None, on_step=None) -> Case:
-    """Run ``paths`` (subset of "eager", "log", "log-replay") over the workload.
+    """Run ``paths`` (subset of "eager", "log", "log-replay", "log-fused") over the workload.
+
+    "log" merges a full log with the WY merge after the step that fills it,
+    "log-replay" with the replay merge, "log-fused" inside that step.
 
     ``pairs``: selected flat pair indices (unit_total * H + head) to record;
     None records all.  ``on_step(tau, states)`` is called after each step.
@@ -62,7 +65,8 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
     for path in paths:
         per_layer = []
         for l in range(layers):
-            st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype)
+            st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype,
+                               merge_on_step=(path == "log-fused"))
             st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
             per_layer.append(st)
         states[path] = per_layer

@@ -76,6 +76,7 @@ def test_state_bytes_full_size_configs():
     ((0, 4, 2, 128, 64, 8, B.DL_BF16), B.DL_ERR_UNSUPPORTED),   # d_k != d_v
     ((0, 4, 2, 96, 96, 8, B.DL_BF16), B.DL_ERR_UNSUPPORTED),    # d not built
     ((0, 4, 2, 128, 128, 65, B.DL_BF16), B.DL_ERR_UNSUPPORTED), # L too long
+    ((0, 4, 2, 128, 128, 8, B.DL_BF16, 2), B.DL_ERR_INVALID),   # merge_on_step not 0 / 1
 ])
 def test_bad_descriptors(lib, fields, code):
     desc = B.DlDesc(*fields)

@@ -35,7 +35,8 @@ def _bits(t):
     (W.KDA_SWEEP.scaled(batch=3, heads=2, steps=11, ragged=True), 3),
     (W.RWKV6_ADD.scaled(batch=3, heads=2, steps=9, ragged=True), 5),
 ])
-def test_schedule_and_payload_bit_exact(wl, L):
+@pytest.mark.parametrize("path", ["log", "log-fused"])
+def test_schedule_and_payload_bit_exact(wl, L, path):
     """After every step: fill == (tokens so far) mod L for every head, and the
     slot written holds bit copies of that step's k, v and beta, and the decay
     accumulated through it."""
@@ -43,7 +44,7 @@ def test_schedule_and_payload_bit_exact(wl, L):
     log(f"case schedule {wl.name} L={L} offsets={L - 1 - first}")
 
     def on_step(tau, states):
-        st = states["log"][0]
+        st = states[path][0]
         s = W.draw_step(wl, tau)
         fill = st.fill.cpu().numpy()
         for b in range(wl.batch):
@@ -64,7 +65,7 @@ def test_schedule_and_payload_bit_exact(wl, L):
             if s.beta is not None:
                 assert np.array_equal(st.log_beta[b, :, slot].cpu().numpy(), s.beta[b])
 
-    run_case(wl, L, ("log",), merge_every_step=True, run_oracle=False, on_step=on_step)
+    run_case(wl, L, (path,), merge_every_step=True, run_oracle=False, on_step=on_step)
 
 
 @pytest.mark.parametrize("wl", [W.GDN_HYBRID.scaled(batch=2, heads=3, steps=20),

@@ -17,7 +17,7 @@ from gpu_harness import assert_parity, log, run_case
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ("eager", "log", "log-replay")
+PATHS = ("eager", "log", "log-replay", "log-fused")
 
 
 def test_tiny_gdn_full_config():

@@ -410,7 +410,11 @@ def main(argv=None):
                      "batch": Bt, "layers": layers, "heads": H, "d_k": d, "d_v": wl.d_v,
                      "log_len": L, "input_dtype": wl.dtype, "state_dtype": "fp32",
                      "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix}
-    main_path = next((p for p in ("log-fused", "log") if p in results), paths[0])
+    # the DeltaLog figure is the faster of the two merge schedules measured
+    # here (both are reported): the merge launched after the step that
+    # fills a log, or merged inside that step
+    logs = [p for p in ("log", "log-fused") if p in results]
+    main_path = max(logs, key=lambda p: results[p]["updates_per_s"]) if logs else paths[0]
     r = results[main_path]
     out["value"] = r["updates_per_s"]
     out["ms_per_step"] = r["ms_per_step"]
@@ -432,13 +436,17 @@ def main(argv=None):
                         "algorithmic_bytes_per_launch": e["step_bytes_per_launch"],
                         "traffic": counter_traffic("eager_step_kernel", wl.name)}
         out["speedup_vs_eager"] = r["updates_per_s"] / e["updates_per_s"]
-    if main_path != "log" and "log" in results:
-        u = results["log"]
-        out["log_separate_merge"] = {"value": u["updates_per_s"], "ms_per_step": u["ms_per_step"],
-                                     "kernel": "log_step_kernel", "achieved_GBps": u["step_kernel_GBps"],
-                                     "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS,
-                                     "avg_launch_us": u["step_kernel_avg_us"],
-                                     "traffic": counter_traffic("log_step_kernel", wl.name)}
+    for other in logs:
+        if other == main_path:
+            continue
+        u = results[other]
+        kn = "log_step_kernel.fused" if other == "log-fused" else "log_step_kernel"
+        out["other_schedule"] = {"path": other, "value": u["updates_per_s"], "ms_per_step": u["ms_per_step"],
+                                 "kernel": kn, "achieved_GBps": u["step_kernel_GBps"],
+                                 "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS,
+                                 "avg_launch_us": u["step_kernel_avg_us"],
+                                 "algorithmic_bytes_per_launch": u["step_bytes_per_launch"],
+                                 "traffic": counter_traffic(kn, wl.name)}
     if "log" in results and results["log"]["merge_launches"]:
         u = results["log"]
         ms = u["merge_ms_total"] / 1e3

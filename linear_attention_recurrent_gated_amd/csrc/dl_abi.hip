@@ -206,9 +206,9 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.dtype = desc->in_dtype;
     p.flags = reinterpret_cast<int *>(m + l.off_flags);
     p.fuse = desc->merge_on_step;
-    // stream the state when the base is more than half of MI355X's 256 MiB
-    // Infinity Cache: such a state set cannot stay resident between calls
-    p.stream = (size_t)desc->units * desc->heads * desc->d_v * desc->d_k * 4 > ((size_t)128 << 20);
+    // stream the state when the base is larger than MI355X's 256 MiB Infinity
+    // Cache: such a state set cannot stay resident between calls
+    p.stream = (size_t)desc->units * desc->heads * desc->d_v * desc->d_k * 4 > ((size_t)256 << 20);
     p.fill = reinterpret_cast<int *>(m + l.off_fill);
     p.base = reinterpret_cast<float *>(m + l.off_base);
     const bool has_log = desc->log_len > 0;

@@ -204,6 +204,23 @@ const char *dl_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */
 int32_t dl_version(void);
 
+/* Log length with the lowest modeled cost per state update for the shape in
+ * `desc` (variant, d_k, d_v, in_dtype, merge_on_step; desc->log_len and the
+ * unit and head counts are ignored).  The model is the traffic the method
+ * must move per update -- the base read, the logged entries read back, the
+ * append, the key-side factors and the amortised merge (one base write per L
+ * steps when merge_on_step is set, else a separate read + write of the base
+ * and the log) -- divided by the share of its bandwidth-bound rate the step
+ * kernel keeps at that L: it needs four workgroups per CU, and fewer fit once
+ * the staged log outgrows a quarter of the CU's 160 KiB LDS.  This is the
+ * merge-interval trade-off of the DeltaLog page's Traffic Model, made
+ * concrete for this kernel.  Candidates are 1..64; ties go to the smaller L.
+ * Writes the choice to *L_out and, if bytes_out is not NULL, the modeled
+ * bytes per update (before the occupancy factor) to *bytes_out.
+ * Errors: DL_ERR_INVALID / DL_ERR_UNSUPPORTED as dl_state_bytes would report
+ * for the descriptor with log_len = 1, or a NULL L_out. */
+dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_out);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,8 @@ _SIGS = {
     "dl_time_next_launch": (_I, [_P, _P, _P]),
     "dl_last_error": (ctypes.c_char_p, []),
     "dl_version": (_I, []),
+    "dl_suggest_log_len": (_I, [ctypes.POINTER(DlDesc), ctypes.POINTER(ctypes.c_int32),
+                                ctypes.POINTER(ctypes.c_double)]),
 }
 
 _lib = None
@@ -103,6 +105,16 @@ def dl_last_error() -> str:
 
 def dl_version() -> int:
     return int(load().dl_version())
+
+
+def dl_suggest_log_len(desc: DlDesc):
+    """(L, modeled bytes per update) with the lowest modeled cost for this shape."""
+    L = ctypes.c_int32(0)
+    b = ctypes.c_double(0.0)
+    rc = load().dl_suggest_log_len(ctypes.byref(desc), ctypes.byref(L), ctypes.byref(b))
+    if rc != DL_OK:
+        raise DlError(rc, dl_last_error())
+    return int(L.value), float(b.value)
 
 
 def dl_state_bytes(desc: DlDesc) -> int:

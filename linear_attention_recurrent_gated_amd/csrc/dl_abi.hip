@@ -8,6 +8,8 @@
 
 #include <new>
 
+#include <algorithm>
+
 #include "dl_common.hpp"
 
 struct dl_state {
@@ -357,5 +359,45 @@ dl_status dl_time_next_launch(dl_state *st, void *start_event, void *stop_event)
 const char *dl_last_error(void) { return g_err; }
 
 int32_t dl_version(void) { return 100; }
+
+dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_out) {
+    if (!desc || !L_out)
+        return fail(DL_ERR_INVALID, "desc and L_out must be non-NULL");
+    dl_desc d = *desc;
+    d.log_len = 1;
+    const dl_status cs = check_desc(&d);
+    if (cs != DL_OK)
+        return cs;
+    const double es = d.in_dtype == DL_BF16 ? 2.0 : 4.0;
+    const double dk = d.d_k, dv = d.d_v;
+    const double St = 4.0 * dv * dk;
+    const double gb = d.variant == DL_GDN ? 4.0 : 4.0 * dk;       // decay bytes per entry
+    const double bb = d.variant == DL_RWKV6 ? 0.0 : 4.0;          // beta bytes per entry
+    const double In = (2.0 * dk + dv) * es + gb + bb;
+    const double Out = 4.0 * dv;
+    const double E = (dk + dv) * es + gb + bb;
+    const bool delta = d.variant != DL_RWKV6;
+    const bool fuse = d.merge_on_step != 0;
+    int best = 1;
+    double best_cost = 0.0, best_bytes = 0.0;
+    for (int L = 1; L <= 64; ++L) {
+        const double c = (L - 1) / 2.0;                           // mean logged entries read
+        const double rt = delta ? 4.0 * ((L - 1.0) * (L - 2.0) / 6.0 + c) : 0.0;
+        double bytes = St + c * E + E + In + Out + 8.0 + rt;
+        bytes += fuse ? St / L : (2.0 * St + L * E + 8.0) / L;
+        const int lds = dl::step_plan(d.variant, d.d_k, (int)es, L, fuse).bytes;
+        const int wgs = std::min(4, (160 * 1024) / std::max(lds, 1));
+        const double cost = bytes * 4.0 / std::max(wgs, 1);
+        if (L == 1 || cost < best_cost) {
+            best = L;
+            best_cost = cost;
+            best_bytes = bytes;
+        }
+    }
+    *L_out = best;
+    if (bytes_out)
+        *bytes_out = best_bytes;
+    return ok();
+}
 
 }  // extern "C"

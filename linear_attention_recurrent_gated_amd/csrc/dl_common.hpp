@@ -48,6 +48,14 @@ struct Shape {
 };
 
 __device__ __forceinline__ int col_of(int s, int m, int e) { return 4 * s + 32 * m + e; }
+// v_mfma_f32_16x16x4_f32: D(16x16) += A(16x4) B(4x16); lane l supplies
+// A[l % 16][l / 16] and B[l / 16][l % 16] and holds D[4 (l / 16) + r][l % 16].
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // State tiles.  When a call's states are larger than the last-level cache
 // can usefully hold (NT), every state is read (and written) once per kernel
 // with the nontemporal hint: the lines do not displace reusable data and the

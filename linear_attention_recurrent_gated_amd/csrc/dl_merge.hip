@@ -31,11 +31,6 @@
 
 namespace dl {
 
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ floatx4 mfma16x16x4(float a, float b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 __device__ __forceinline__ bool resolve_merge_pair(const Params &P, const int *slot_idx, int mode,
                                                    size_t &pair, int &n) {

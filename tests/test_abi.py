@@ -112,3 +112,31 @@ def test_null_handle_is_rejected(lib):
     assert lib.dl_state_view(None, None) == B.DL_ERR_INVALID
     assert lib.dl_state_free(None) == B.DL_OK
     assert B.dl_version() == 100
+
+
+@pytest.mark.parametrize("variant,d,dt,fuse", [(B.DL_GDN, 128, B.DL_BF16, 1), (B.DL_KDA, 128, B.DL_BF16, 1),
+                                               (B.DL_KDA, 128, B.DL_BF16, 0), (B.DL_RWKV6, 64, B.DL_BF16, 0),
+                                               (B.DL_GDN, 64, B.DL_F32, 0)])
+def test_suggest_log_len(lib, variant, d, dt, fuse):
+    """The suggested L is the argmin of the documented traffic model, and its
+    modeled bytes undercut both extremes (merge every step, longest log)."""
+    desc = B.DlDesc(variant, 1, 1, d, d, 0, dt, fuse)
+    L, b = B.dl_suggest_log_len(desc)
+    assert 1 < L < 64
+    es = 2 if dt == B.DL_BF16 else 4
+    St, g, bb = 4 * d * d, (4 if variant == B.DL_GDN else 4 * d), (0 if variant == B.DL_RWKV6 else 4)
+    In, Out, E = 3 * d * es + g + bb, 4 * d, 2 * d * es + g + bb
+
+    def model(L):
+        c = (L - 1) / 2
+        rt = 4 * ((L - 1) * (L - 2) / 6 + c) if variant != B.DL_RWKV6 else 0
+        x = St + c * E + E + In + Out + 8 + rt
+        return x + (St / L if fuse else (2 * St + L * E + 8) / L)
+
+    assert b == pytest.approx(model(L), rel=1e-12)
+    assert b < model(1) and b < model(64)
+
+
+def test_suggest_log_len_errors(lib):
+    with pytest.raises(B.DlError):
+        B.dl_suggest_log_len(B.DlDesc(0, 1, 1, 96, 96, 0, B.DL_BF16))

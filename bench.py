@@ -268,22 +268,45 @@ def main(argv=None):
         lib = B.load()
         step_fn = lib.dl_decode_step_eager if path == "eager" else lib.dl_decode_step_log
         fills = np.zeros(Bt, dtype=np.int64)     # host model of each sequence's log fill
-        keep = []                                # gathered inputs of ragged prefix steps
+        keep = []                                # device buffers the plan points into
+        prefix_out = []                          # gathered inputs / outputs of ragged prefix steps
 
         # every launch of the run, with its arguments, decided before anything runs
         plan = []                                # (tau, kind, handle, args)
+        scatter = []                             # (o, l, tau, row order) of reordered steps
         for tau in range(T):
+            # the serving loop knows which logs fill at this step (the host model
+            # of the schedule): with ragged logs it merges only those units, and
+            # when the step merges in place it puts them first in the batch so
+            # their longer workgroups start early instead of trailing the launch
+            full_next = np.nonzero(fills + np.isin(np.arange(Bt), act[tau]) == L)[0]
+            order = None
+            if wl.ragged and tau >= prefix and path == "log-fused" and 0 < len(full_next) < Bt:
+                rest = np.setdiff1d(np.arange(Bt), full_next)
+                order = np.concatenate([full_next, rest])
+                order_t = torch.from_numpy(order.astype(np.int64)).to(dev)
+                slot_o = torch.from_numpy(order.astype(np.int32)).to(dev)
+            merge_slots = None
+            if wl.ragged and path == "log" and len(full_next):
+                merge_slots = torch.from_numpy(full_next.astype(np.int32)).to(dev)
             for l in range(layers):
                 st = states[l]
                 lo, hi = l * Bt, (l + 1) * Bt
                 if len(act[tau]) == 0:
                     continue
-                if tau in gathers:
+                if order is not None:
+                    xs = [x[tau, lo:hi].index_select(0, order_t).contiguous() for x in (Q, Kt, V, G)]
+                    xs.append(Bb[tau, lo:hi].index_select(0, order_t).contiguous() if Bb is not None else None)
+                    o = torch.empty((Bt, H, d), dtype=torch.float32, device=dev)
+                    keep.append((xs, slot_o))
+                    scatter.append((o, l, tau, order_t))
+                    rows, sp = Bt, slot_o.data_ptr()
+                elif tau in gathers:
                     idx, slot, rows = gathers[tau]
                     xs = [x[tau, lo:hi].index_select(0, idx).contiguous() for x in (Q, Kt, V, G)]
                     xs.append(Bb[tau, lo:hi].index_select(0, idx).contiguous() if Bb is not None else None)
                     o = torch.empty((rows, H, d), dtype=torch.float32, device=dev)
-                    keep.append((xs, o, l, tau))
+                    prefix_out.append((xs, o, l, tau))
                     sp = slot.data_ptr()
                 else:
                     xs = [Q[tau, lo:hi], Kt[tau, lo:hi], V[tau, lo:hi], G[tau, lo:hi],
@@ -294,7 +317,11 @@ def main(argv=None):
                 if path != "eager":
                     if l == 0:
                         fills[act[tau]] += 1
-                    if path == "log" and (wl.ragged or np.any(fills == L)):
+                    if path == "log" and merge_slots is not None:
+                        keep.append(merge_slots)
+                        plan.append((tau, "merge", st.handle,
+                                     (len(full_next), merge_slots.data_ptr(), B.DL_MERGE_FULL, stream)))
+                    elif path == "log" and np.any(fills == L):
                         plan.append((tau, "merge", st.handle, (Bt, None, B.DL_MERGE_FULL, stream)))
                     if l == layers - 1:
                         fills[fills == L] = 0
@@ -312,7 +339,7 @@ def main(argv=None):
                     raise RuntimeError(f"{kind} failed: {B.dl_last_error()}")
 
         run([(kind, h, a) for tau, kind, h, a in plan if tau < t_first])
-        for xs, o, l, tau in keep:
+        for xs, o, l, tau in prefix_out:
             O[tau, l * Bt:(l + 1) * Bt].index_copy_(0, gathers[tau][0], o)
         fills_at_start = np.zeros(Bt, dtype=np.int64)
         for tau in range(t_first):
@@ -362,8 +389,9 @@ def main(argv=None):
                     if l == layers - 1:
                         f += 1
                         full = f == L
-                        if path == "log" and (wl.ragged or full.any()):   # a merge launch followed
-                            mbytes += layers * H * (merge_bytes(m, L) * full.sum() + 4 * (~full).sum())
+                        if path == "log" and full.any():   # a merge launch followed
+                            idle = 0 if wl.ragged else (~full).sum()   # ragged: only full units launched
+                            mbytes += layers * H * (merge_bytes(m, L) * full.sum() + 4 * idle)
                             mflops += layers * H * merge_flops(wl, L) * full.sum()
                         f[full] = 0
         kern_s = sum(step_ms) / 1e3
@@ -380,6 +408,8 @@ def main(argv=None):
             merge_bytes=mbytes,
             merge_flops=mflops,
         )
+        for o, l, tau, order_t in scatter:       # back to batch order
+            O[tau, l * Bt:(l + 1) * Bt].index_copy_(0, order_t, o)
         # sampled outputs and final states for the parity check
         su, sh = torch.from_numpy(sample // H).to(dev), torch.from_numpy(sample % H).to(dev)
         res["o_sample"] = O[:, su, sh].double().cpu().numpy()            # [T, n, d]

@@ -9,6 +9,8 @@ falls back to it.
   independent states; ``recurrence.c``).  It follows the operator list of the
   DeltaLog page (Technical Summary, Kernel Implementation) with the update
   formulas written out in ``recurrence.c``.
+* :func:`additive_factor` -- the per-step factor ``a_t`` that an
+  additive-factor log stores (numpy, float64).
 * :mod:`oracle.exact` -- exact rational (``fractions.Fraction``) models used
   to pin the float64 oracle and the deferred base + log algebra.
 
@@ -109,6 +111,30 @@ def readout(S, q):
     S = np.asarray(S, dtype=np.float64)
     q = np.asarray(q, dtype=np.float64)
     return np.einsum("pij,pj->pi", S, q)
+
+
+def additive_factor(variant: int, S_prev, k, v, g, beta=None):
+    """The compact update factor ``a_t`` of one step, in float64.
+
+    A step writes ``S_t = S_{t-1} diag(alpha_t) + a_t k_t^T`` with
+    ``alpha_t = exp(g_t)`` (a scalar for the head-wise decay) and
+    ``a_t = beta_t (v_t - S_{t-1} (alpha_t * k_t))`` for the delta-rule
+    operators, ``a_t = v_t`` for the additive one: the factor pair
+    ``(a_t, b_t = k_t)`` that the DeltaLog page's Core Mechanism appends to
+    the log instead of writing the state.
+
+    Shapes: ``S_prev`` ``[P, d_v, d_k]``; ``k`` ``[P, d_k]``; ``v`` ``[P, d_v]``;
+    ``g`` ``[P]`` or ``[P, d_k]``; ``beta`` ``[P]``.  Returns ``[P, d_v]``.
+    """
+    S = np.asarray(S_prev, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if variant == RWKV6:
+        return v.copy()
+    g = np.asarray(g, dtype=np.float64)
+    alpha = np.exp(g)[:, None] if variant == GDN else np.exp(g)
+    x = np.einsum("pij,pj->pi", S, alpha * k)
+    return np.asarray(beta, dtype=np.float64)[:, None] * (v - x)
 
 
 def max_threads() -> int:

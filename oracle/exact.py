@@ -20,6 +20,9 @@ Sources:
   base plus log and resets the log -- is the DeltaLog page's Core Mechanism;
   its claim that this only changes the physical schedule, not the
   recurrence (Methodology), is what :func:`deferred_run` is tested against;
+* the additive-factor log (``af_*``) stores the compact factors
+  ``(a_t, b_t)`` and the decay snapshot that the Core Mechanism names, with
+  ``a_t`` the delta-rule write ``beta_t (v_t - S_{t-1}(alpha_t * k_t))``;
 * the merge is written in WY/UT form: a product of rank-one delta-rule
   transforms folded into one triangular solve, the block form the CARVE page
   (abstract) and its Gated DeltaNet-2 neighbour (chunkwise WY algorithm)
@@ -260,6 +263,49 @@ def wy_readout(variant, base, log, q):
     return o
 
 
+def wy_solve_u(variant, base, log):
+    """Columns ``U_j`` of the WY merge's triangular solve (see :func:`wy_merge`).
+
+    ``W_j = base (k_j * P_j)``, ``M_ij = beta_j sum_c k_i[c] k_j[c] D(i, j)[c]``
+    (``i < j``), and ``U (I + M) = (V - W) diag(beta)`` by forward
+    substitution over columns; RWKV6: ``U = V``.
+    """
+    n = len(log)
+    dk = len(log[0][0])
+    decays = [_chan(variant, e[2], dk) for e in log]
+    P = []
+    acc = [Fr(1)] * dk
+    for a in decays:
+        acc = [x * y for x, y in zip(acc, a)]
+        P.append(acc)
+
+    def D(i, j):  # product of decays of entries i+1..j
+        out = [Fr(1)] * dk
+        for m in range(i + 1, j + 1):
+            out = [x * y for x, y in zip(out, decays[m])]
+        return out
+
+    ks = [[Fr(x) for x in e[0]] for e in log]
+    vs = [[Fr(x) for x in e[1]] for e in log]
+    if variant == RWKV6:
+        return vs
+    betas = [Fr(e[3]) for e in log]
+    W = [matvec(base, [kk * p for kk, p in zip(ks[j], P[j])]) for j in range(n)]
+    M = [[Fr(0)] * n for _ in range(n)]
+    for i in range(n):
+        for j in range(i + 1, n):
+            dij = D(i, j)
+            M[i][j] = betas[j] * sum((a * b * c for a, b, c in zip(ks[i], ks[j], dij)), Fr(0))
+    B = [[betas[j] * (vv - ww) for vv, ww in zip(vs[j], W[j])] for j in range(n)]
+    U = []
+    for j in range(n):
+        col = list(B[j])
+        for i in range(j):
+            col = [c - u * M[i][j] for c, u in zip(col, U[i])]
+        U.append(col)
+    return U
+
+
 def wy_merge(variant, base, log):
     """Materialise ``base`` followed by the logged updates in WY/UT form.
 
@@ -292,24 +338,7 @@ def wy_merge(variant, base, log):
         return out
 
     ks = [[Fr(x) for x in e[0]] for e in log]
-    vs = [[Fr(x) for x in e[1]] for e in log]
-    if variant == RWKV6:
-        U = vs
-    else:
-        betas = [Fr(e[3]) for e in log]
-        W = [matvec(base, [kk * p for kk, p in zip(ks[j], P[j])]) for j in range(n)]
-        M = [[Fr(0)] * n for _ in range(n)]
-        for i in range(n):
-            for j in range(i + 1, n):
-                dij = D(i, j)
-                M[i][j] = betas[j] * sum((a * b * c for a, b, c in zip(ks[i], ks[j], dij)), Fr(0))
-        B = [[betas[j] * (vv - ww) for vv, ww in zip(vs[j], W[j])] for j in range(n)]
-        U = []
-        for j in range(n):
-            col = list(B[j])
-            for i in range(j):
-                col = [c - u * M[i][j] for c, u in zip(col, U[i])]
-            U.append(col)
+    U = wy_solve_u(variant, base, log)
     last = n - 1
     S = [[x * p for x, p in zip(row, P[last])] for row in base]
     for j in range(n):
@@ -338,6 +367,78 @@ def deferred_run(variant, S0, qs, ks, vs, alphas, betas, L):
             log = []
     fill = len(log)
     return outs, wy_merge(variant, base, log), fill
+
+
+# ----------------------------------------------------------------------------
+# additive-factor log
+# ----------------------------------------------------------------------------
+def af_append(variant, base, log, k, v, alpha, beta):
+    """The next entry ``(a, b, P)`` of an additive-factor log.
+
+    The log stands for the state ``base diag(P_c) + sum_j a_j (b_j * P_c / P_j)^T``
+    (``P_j`` the decay accumulated over entries ``0..j``, ``c`` the newest):
+    the dense base plus decayed rank-one terms, i.e. the compact update
+    factors ``(a_t, b_t)`` with their log-decay snapshot of the DeltaLog
+    page's Core Mechanism.  For a step with ``(k, v, alpha, beta)``:
+    ``P_n = P_{n-1} * alpha``, ``b = k`` and ``a = beta (v - x)`` with
+    ``x = S_{n-1} (alpha * k) = base (P_n * k) + sum_{j<n} a_j (b_j * P_n / P_j) . k``,
+    read from base and log without materialising ``S_{n-1}`` (RWKV6: ``a = v``).
+    """
+    dk = len(k)
+    prev = log[-1][2] if log else [Fr(1)] * dk
+    Pn = [x * y for x, y in zip(prev, _chan(variant, alpha, dk))]
+    kf = [Fr(x) for x in k]
+    vf = [Fr(x) for x in v]
+    if variant == RWKV6:
+        return (vf, kf, Pn)
+    x = matvec(base, [p * kk for p, kk in zip(Pn, kf)])
+    for a, b, Pj in log:
+        u = sum((bb * p / pj * kk for bb, p, pj, kk in zip(b, Pn, Pj, kf)), Fr(0))
+        x = [xi + u * ai for xi, ai in zip(x, a)]
+    return ([Fr(beta) * (vi - xi) for vi, xi in zip(vf, x)], kf, Pn)
+
+
+def af_readout(base, log, q):
+    """``o = base (P_c * q) + sum_j a_j ((b_j * P_c / P_j) . q)``: independent
+    dot products per entry, no triangular solve and no chain."""
+    qf = [Fr(x) for x in q]
+    if not log:
+        return matvec(base, qf)
+    Pc = log[-1][2]
+    o = matvec(base, [p * x for p, x in zip(Pc, qf)])
+    for a, b, Pj in log:
+        r = sum((bb * p / pj * x for bb, p, pj, x in zip(b, Pc, Pj, qf)), Fr(0))
+        o = [oi + r * ai for oi, ai in zip(o, a)]
+    return o
+
+
+def af_merge(base, log):
+    """``base diag(P_c) + sum_j a_j (b_j * P_c / P_j)^T``: one contraction."""
+    if not log:
+        return [list(r) for r in base]
+    Pc = log[-1][2]
+    S = [[x * p for x, p in zip(row, Pc)] for row in base]
+    for a, b, Pj in log:
+        S = madd(S, outer(a, [bb * p / pj for bb, p, pj in zip(b, Pc, Pj)]))
+    return S
+
+
+def af_deferred_run(variant, S0, qs, ks, vs, alphas, betas, L):
+    """:func:`deferred_run` with the additive-factor log: every step appends
+    ``(a, b, P)`` and reads out with every entry (the new one included);
+    a full log is merged and emptied.  Returns ``(outputs, final state, fill,
+    every appended factor a in order)``."""
+    base = [list(r) for r in S0]
+    log, outs, factors = [], [], []
+    for t in range(len(ks)):
+        b = None if betas is None else betas[t]
+        log.append(af_append(variant, base, log, ks[t], vs[t], alphas[t], b))
+        factors.append(log[-1][0])
+        outs.append(af_readout(base, log, qs[t]))
+        if len(log) == L:
+            base = af_merge(base, log)
+            log = []
+    return outs, af_merge(base, log), len(log), factors
 
 
 def compact_wy_T(betas, ks):

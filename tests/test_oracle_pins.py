@@ -157,3 +157,63 @@ def test_wy_r_is_inverse_of_unit_triangular(variant):
             Nm[i][j] = u[i]
     I_plus_N = exact.madd(exact.eye(n), Nm)
     assert exact.matmul(I_plus_N, R) == exact.eye(n)
+
+
+# ----------------------------------------------------------------------------
+# additive-factor log
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("L", [1, 2, 3, 5])
+def test_af_deferred_equals_eager_exactly(variant, L):
+    """Base + additive-factor log (append, readout, merge) == the eager recurrence, exactly."""
+    rng = np.random.default_rng(500 + 10 * variant + L)
+    T, d = 8, 3
+    S0, qs, ks, vs, alphas, betas = _exact_case(variant, rng, T, d)
+    o_e, S_e = exact.run_stepwise(variant, S0, qs, ks, vs, alphas, betas)
+    o_d, S_d, fill, _ = exact.af_deferred_run(variant, S0, qs, ks, vs, alphas, betas, L)
+    assert o_d == o_e
+    assert S_d == S_e
+    assert fill == T % L
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_af_factors_are_wy_solve_columns(variant):
+    """The factors appended step by step equal the columns of the WY merge's
+    triangular solve over the same entries: two derivations, one result."""
+    rng = np.random.default_rng(600 + variant)
+    n, d = 6, 4
+    S0, qs, ks, vs, alphas, betas = _exact_case(variant, rng, n, d)
+    _, _, _, factors = exact.af_deferred_run(variant, S0, qs, ks, vs, alphas, betas, n + 1)
+    log = [(ks[j], vs[j], alphas[j], None if betas is None else betas[j]) for j in range(n)]
+    assert factors == exact.wy_solve_u(variant, S0, log)
+
+
+def test_additive_factor_against_recurrence_and_exact_model():
+    """oracle.additive_factor: S_1 - S_0 diag(alpha) = a k^T for one step of the
+    C oracle, and a equals the exact model's factor on float inputs."""
+    rng = np.random.default_rng(14)
+    P, d = 5, 4
+    for variant in VARIANTS:
+        S0 = rng.standard_normal((P, d, d)).astype(np.float32)
+        q, k, v = (rng.standard_normal((1, P, d)).astype(np.float32) for _ in range(3))
+        g = (-rng.random((1, P) if variant == GDN else (1, P, d))).astype(np.float32)
+        beta = None if variant == RWKV6 else rng.random((1, P)).astype(np.float32)
+        _, S1 = oracle.run(variant, q, k, v, g, beta, S0)
+        a = oracle.additive_factor(variant, S0, k[0], v[0], g[0], None if beta is None else beta[0])
+        alpha = np.exp(g[0].astype(np.float64))
+        decayed = S0 * (alpha[:, None, None] if variant == GDN else alpha[:, None, :])
+        resid = S1 - decayed - a[:, :, None] * k[0].astype(np.float64)[:, None, :]
+        assert np.abs(resid).max() <= 1e-12 * max(1.0, np.abs(S1).max())
+        # exact model on exactly representable inputs
+        S0x = (rng.integers(-4, 5, size=(d, d)) / 4).astype(np.float32)
+        kx, vx = ((rng.integers(-8, 9, size=d) / 8).astype(np.float32) for _ in range(2))
+        gx = (-rng.integers(0, 5, size=() if variant == GDN else (d,)) / 8).astype(np.float32)
+        bx = np.float32(rng.integers(0, 9) / 8)
+        alpha_x = Fr(math.exp(float(gx))) if variant == GDN else [Fr(math.exp(float(x))) for x in gx]
+        ax, _, _ = exact.af_append(variant, [[Fr(float(x)) for x in r] for r in S0x], [],
+                                   [Fr(float(x)) for x in kx], [Fr(float(x)) for x in vx],
+                                   alpha_x, Fr(float(bx)))
+        af = oracle.additive_factor(variant, S0x[None], kx[None], vx[None],
+                                    np.asarray(gx)[None], np.asarray([bx]))
+        ref = np.array([float(x) for x in ax])
+        assert np.abs(af[0] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())

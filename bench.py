@@ -54,7 +54,16 @@ def byte_model(wl: W.Workload):
     Out = 4 * dv                                       # fp32 o
     E = (dk + dv) * es + g + b                         # one log entry
     R = 1 if wl.has_beta else 0                        # delta rule: packed R columns
-    return dict(St=St, In=In, Out=Out, E=E, R=R)
+    # additive-factor log (delta rule): key, fp32 factor a_t, decay; no beta, no R
+    E_af = dk * es + 4 * dv + g if wl.has_beta else E
+    return dict(St=St, In=In, Out=Out, E=E, R=R, E_af=E_af)
+
+
+def form_model(m, path):
+    """The byte model of the log form a path uses."""
+    if path.startswith("af"):
+        return dict(m, E=m["E_af"], R=0)
+    return m
 
 
 def eager_bytes(m):
@@ -76,9 +85,10 @@ def merge_bytes(m, n):
     return 2 * m["St"] + n * m["E"] + 8
 
 
-def merge_flops(wl, n):
-    """The two dense contractions per merged state (W = S Kt^T, S += Z Y)."""
-    mult = 1 if wl.variant == W.RWKV6 else 2
+def merge_flops(wl, n, factors=False):
+    """The dense contractions per merged state: W = S Kt^T and S += Z Y (WY),
+    S += A Kd^T alone for the additive-factor log and the additive variant."""
+    mult = 1 if (wl.variant == W.RWKV6 or factors) else 2
     return 2 * wl.d_v * wl.d_k * n * mult
 
 
@@ -122,9 +132,10 @@ def parse_args(argv=None):
     ap.add_argument("--config", type=int, default=2, choices=sorted(W.WORKLOADS))
     ap.add_argument("--L", type=int, default=None, help="log slots (default: the workload's)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--paths", default="eager,log,log-fused",
+    ap.add_argument("--paths", default="eager,log,log-fused,af,af-fused",
                     help="eager; log (merge launched after the step that fills a log); "
-                         "log-fused (that step merges in the same pass)")
+                         "log-fused (that step merges in the same pass); af, af-fused: "
+                         "the same with the additive-factor log (delta-rule variants)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
@@ -193,7 +204,10 @@ def main(argv=None):
     U = wl.units_total
     P = U * H
     paths = args.paths.split(",")
-    m = byte_model(wl)
+    if not wl.has_beta:
+        # the additive variant's log already stores additive factors: af == log
+        paths = [p for p in paths if not p.startswith("af")]
+    m0 = byte_model(wl)
     log(f"[bench] {wl.name}: variant {W.VARIANT_NAMES[wl.variant]}, {P} states, d={d}, L={L}, "
         f"steps {prefix}+{Wu}+{K}, inputs {wl.dtype}")
 
@@ -257,10 +271,14 @@ def main(argv=None):
 
     results = {}
     for path in paths:
+        m = form_model(m0, path)
+        fused = path.endswith("-fused")
+        separate = path in ("log", "af")          # merges launched after the step
         states = []
         for l in range(layers):
             st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype, device=dev,
-                               merge_on_step=(path == "log-fused"))
+                               merge_on_step=fused,
+                               log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY)
             st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
             states.append(st)
         O = torch.zeros((T, U, H, d), dtype=torch.float32, device=dev)
@@ -281,13 +299,13 @@ def main(argv=None):
             # their longer workgroups start early instead of trailing the launch
             full_next = np.nonzero(fills + np.isin(np.arange(Bt), act[tau]) == L)[0]
             order = None
-            if wl.ragged and tau >= prefix and path == "log-fused" and 0 < len(full_next) < Bt:
+            if wl.ragged and tau >= prefix and fused and 0 < len(full_next) < Bt:
                 rest = np.setdiff1d(np.arange(Bt), full_next)
                 order = np.concatenate([full_next, rest])
                 order_t = torch.from_numpy(order.astype(np.int64)).to(dev)
                 slot_o = torch.from_numpy(order.astype(np.int32)).to(dev)
             merge_slots = None
-            if wl.ragged and path == "log" and len(full_next):
+            if wl.ragged and separate and len(full_next):
                 merge_slots = torch.from_numpy(full_next.astype(np.int32)).to(dev)
             for l in range(layers):
                 st = states[l]
@@ -317,11 +335,11 @@ def main(argv=None):
                 if path != "eager":
                     if l == 0:
                         fills[act[tau]] += 1
-                    if path == "log" and merge_slots is not None:
+                    if separate and merge_slots is not None:
                         keep.append(merge_slots)
                         plan.append((tau, "merge", st.handle,
                                      (len(full_next), merge_slots.data_ptr(), B.DL_MERGE_FULL, stream)))
-                    elif path == "log" and np.any(fills == L):
+                    elif separate and np.any(fills == L):
                         plan.append((tau, "merge", st.handle, (Bt, None, B.DL_MERGE_FULL, stream)))
                     if l == layers - 1:
                         fills[fills == L] = 0
@@ -380,7 +398,7 @@ def main(argv=None):
             f = fills_at_start.copy()
             for tau in range(prefix + Wu, T):
                 for l in range(layers):
-                    if path == "log-fused":
+                    if fused:
                         # the step that fills a log also writes the merged base
                         step_bytes.append(float(np.sum([log_step_bytes(m, c) + (m["St"] if c == L - 1 else 0)
                                                         for c in f])) * H)
@@ -389,10 +407,10 @@ def main(argv=None):
                     if l == layers - 1:
                         f += 1
                         full = f == L
-                        if path == "log" and full.any():   # a merge launch followed
+                        if separate and full.any():   # a merge launch followed
                             idle = 0 if wl.ragged else (~full).sum()   # ragged: only full units launched
                             mbytes += layers * H * (merge_bytes(m, L) * full.sum() + 4 * idle)
-                            mflops += layers * H * merge_flops(wl, L) * full.sum()
+                            mflops += layers * H * merge_flops(wl, L, path == "af") * full.sum()
                         f[full] = 0
         kern_s = sum(step_ms) / 1e3
         res = dict(
@@ -440,17 +458,19 @@ def main(argv=None):
                      "batch": Bt, "layers": layers, "heads": H, "d_k": d, "d_v": wl.d_v,
                      "log_len": L, "input_dtype": wl.dtype, "state_dtype": "fp32",
                      "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix}
-    # the DeltaLog figure is the faster of the two merge schedules measured
-    # here (both are reported): the merge launched after the step that
-    # fills a log, or merged inside that step
-    logs = [p for p in ("log", "log-fused") if p in results]
+    # the DeltaLog figure is the fastest of the log forms and merge schedules
+    # measured here (all are reported): the compact-WY log or the
+    # additive-factor log, each with the merge launched after the step that
+    # fills a log or merged inside that step
+    knames = {"log": "log_step_kernel", "log-fused": "log_step_kernel.fused",
+              "af": "af_step_kernel", "af-fused": "af_step_kernel.fused"}
+    logs = [p for p in knames if p in results]
     main_path = max(logs, key=lambda p: results[p]["updates_per_s"]) if logs else paths[0]
     r = results[main_path]
     out["value"] = r["updates_per_s"]
     out["ms_per_step"] = r["ms_per_step"]
     out["path"] = main_path
-    kname = {"log-fused": "log_step_kernel.fused", "log": "log_step_kernel"}.get(main_path,
-                                                                                 "eager_step_kernel")
+    kname = knames.get(main_path, "eager_step_kernel")
     out["roofline"] = {"bound": "hbm", "kernel": kname,
                        "achieved": r["step_kernel_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                        "frac": r["step_kernel_GBps"] / HBM_PEAK_GBPS,
@@ -466,25 +486,33 @@ def main(argv=None):
                         "algorithmic_bytes_per_launch": e["step_bytes_per_launch"],
                         "traffic": counter_traffic("eager_step_kernel", wl.name)}
         out["speedup_vs_eager"] = r["updates_per_s"] / e["updates_per_s"]
+    others = []
     for other in logs:
         if other == main_path:
             continue
         u = results[other]
-        kn = "log_step_kernel.fused" if other == "log-fused" else "log_step_kernel"
-        out["other_schedule"] = {"path": other, "value": u["updates_per_s"], "ms_per_step": u["ms_per_step"],
-                                 "kernel": kn, "achieved_GBps": u["step_kernel_GBps"],
-                                 "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS,
-                                 "avg_launch_us": u["step_kernel_avg_us"],
-                                 "algorithmic_bytes_per_launch": u["step_bytes_per_launch"],
-                                 "traffic": counter_traffic(kn, wl.name)}
-    if "log" in results and results["log"]["merge_launches"]:
-        u = results["log"]
-        ms = u["merge_ms_total"] / 1e3
-        out["merge"] = {"kernel": "merge_wy_kernel", "launches": u["merge_launches"],
-                        "share_of_step_time": u["merge_ms_total"] / u["total_ms"],
-                        "GBps": u["merge_bytes"] / ms / 1e9 if ms else None,
-                        "mfma_TFLOPs": u["merge_flops"] / ms / 1e12 if ms else None,
-                        "mfma_frac": (u["merge_flops"] / ms / 1e12 / FP32_MFMA_PEAK_TFLOPS) if ms else None}
+        kn = knames[other]
+        others.append({"path": other, "value": u["updates_per_s"], "ms_per_step": u["ms_per_step"],
+                       "kernel": kn, "achieved_GBps": u["step_kernel_GBps"],
+                       "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS,
+                       "avg_launch_us": u["step_kernel_avg_us"],
+                       "algorithmic_bytes_per_launch": u["step_bytes_per_launch"],
+                       "traffic": counter_traffic(kn, wl.name)})
+    if others:
+        out["other_paths"] = others
+    merges = {}
+    for sep, mk in (("log", "merge_wy_kernel"), ("af", "af_merge_kernel")):
+        if sep in results and results[sep]["merge_launches"]:
+            u = results[sep]
+            ms = u["merge_ms_total"] / 1e3
+            merges[sep] = {"kernel": mk, "launches": u["merge_launches"],
+                           "share_of_step_time": u["merge_ms_total"] / u["total_ms"],
+                           "GBps": u["merge_bytes"] / ms / 1e9 if ms else None,
+                           "TFLOPs": u["merge_flops"] / ms / 1e12 if ms else None,
+                           "fp32_peak_frac": (u["merge_flops"] / ms / 1e12 / FP32_MFMA_PEAK_TFLOPS)
+                           if ms else None}
+    if merges:
+        out["merge"] = merges
 
     # ---- the oracle on the host cores, same inputs, sampled states
     if not args.no_cpu_baseline:

@@ -68,6 +68,17 @@ typedef enum {
 typedef enum { DL_GDN = 0, DL_KDA = 1, DL_RWKV6 = 2 } dl_variant;
 typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
 
+/* What the log stores per pending step (dl_desc.log_form). */
+typedef enum {
+    DL_LOG_WY = 0,           /* bit copies of (k, v), beta, the decay and the
+                              * key-side factors R of the compact WY readout */
+    DL_LOG_FACTORS = 1       /* the additive factors (a_t, b_t = k_t) and the
+                              * decay: a_t = beta_t (v_t - S_{t-1}(alpha_t k_t)),
+                              * fp32; RWKV6's raw-value log is already of this
+                              * form (a_t = v_t), so both values give it the
+                              * same log */
+} dl_log_form;
+
 typedef enum {
     DL_MERGE_FULL = 0,       /* merge units whose log holds exactly L entries */
     DL_MERGE_ALL = 1         /* merge every unit with a non-empty log (flush) */
@@ -90,21 +101,24 @@ typedef struct {
     int32_t merge_on_step; /* 0: a full log waits for dl_merge; 1: the log step
                             * that fills a log also merges it into the base in
                             * the same pass and leaves fill at 0 */
+    int32_t log_form;  /* dl_log_form */
 } dl_desc;
 
 /* Device pointers into a state block (all row-major, contiguous).
  *   base     [units, H, d_v, d_k] fp32  -- the dense state (eager) or base (DeltaLog)
  *   log_k    [units, H, L, d_k] in_dtype -- logged keys, bit copies of the inputs
- *   log_v    [units, H, L, d_v] in_dtype -- logged values
+ *   log_v    [units, H, L, d_v] in_dtype -- logged values; under DL_LOG_FACTORS
+ *            (GDN, KDA) fp32 -- the factors a_t
  *   log_g    [units, H, L] (GDN) or [units, H, L, d_k] (KDA, RWKV6) fp32 -- the
  *            log-decay accumulated from the log's first entry through each
  *            entry (Lam_j = Lam_{j-1} + g_j in fp32, Lam_{-1} = 0)
- *   log_beta [units, H, L] fp32 (NULL for RWKV6)
+ *   log_beta [units, H, L] fp32 (NULL for RWKV6 and under DL_LOG_FACTORS)
  *   log_t    [units, H, L(L-1)/2] fp32 -- key-side factors of the log (delta-
  *            rule variants): the inverse R of the unit upper-triangular
  *            coupling matrix of the logged entries, column j (rows 0..j-1)
  *            at offset j(j-1)/2, written when entry j is appended and read
- *            by every readout (NULL for RWKV6 and when L < 2)
+ *            by every readout (NULL for RWKV6, under DL_LOG_FACTORS and
+ *            when L < 2)
  *   fill     [units, H] int32 -- entries in each log; every head of a unit
  *            advances together, one writer per counter
  *   flags    [1] int32 -- DL_FLAG_* bits
@@ -156,7 +170,9 @@ dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_i
 /* DeltaLog step (the page's Append Phase): append (k, v, g, beta) to slot
  * fill of each row's log without writing the base, then read out
  * o = S_logical q from the read-only base plus the log, the new entry
- * included.  When the log now holds L entries it is full: call dl_merge
+ * included.  Under DL_LOG_FACTORS the entry is (a_t, k_t, the decay), with
+ * a_t read from base + log in the same pass; the readout is then base
+ * (E q) plus one independent dot product per entry.  When the log now holds L entries it is full: call dl_merge
  * (DL_MERGE_FULL) before the unit's next step, or that step is skipped with
  * DL_FLAG_LOG_FULL.  Arguments as for dl_decode_step_eager; needs L >= 1. */
 dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx,
@@ -169,13 +185,16 @@ dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx
  * applied in WY/UT form -- the logged rank-one transforms folded into one
  * triangular solve and two dense contractions on the matrix cores -- the
  * block form the CARVE page (abstract) and Gated DeltaNet-2 (chunkwise WY
- * algorithm) use. */
+ * algorithm) use.  Under DL_LOG_FACTORS the log already holds the solved
+ * factors: base' = base diag(E_c) + sum_j a_j (k_j E_c / E_j)^T, one
+ * contraction. */
 dl_status dl_merge(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
                    void *stream);
 
 /* Same result as dl_merge, computed by replaying the logged steps one by
  * one on the vector ALUs (a cross-check of the WY path; also a fallback for
- * callers who prefer its rounding). */
+ * callers who prefer its rounding).  Under DL_LOG_FACTORS there is nothing
+ * to replay: the same contraction as dl_merge. */
 dl_status dl_merge_replay(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
                           void *stream);
 
@@ -205,8 +224,8 @@ const char *dl_last_error(void);
 int32_t dl_version(void);
 
 /* Log length with the lowest modeled cost per state update for the shape in
- * `desc` (variant, d_k, d_v, in_dtype, merge_on_step; desc->log_len and the
- * unit and head counts are ignored).  The model is the traffic the method
+ * `desc` (variant, d_k, d_v, in_dtype, merge_on_step, log_form;
+ * desc->log_len and the unit and head counts are ignored).  The model is the traffic the method
  * must move per update -- the base read, the logged entries read back, the
  * append, the key-side factors and the amortised merge (one base write per L
  * steps when merge_on_step is set, else a separate read + write of the base

@@ -22,6 +22,7 @@ DL_OK, DL_ERR_INVALID, DL_ERR_UNSUPPORTED, DL_ERR_SIZE, DL_ERR_LAUNCH, DL_ERR_ST
 DL_GDN, DL_KDA, DL_RWKV6 = 0, 1, 2
 DL_F32, DL_BF16 = 0, 1
 DL_MERGE_FULL, DL_MERGE_ALL = 0, 1
+DL_LOG_WY, DL_LOG_FACTORS = 0, 1
 DL_FLAG_LOG_FULL, DL_FLAG_LOG_NONEMPTY, DL_FLAG_BAD_SLOT = 1, 2, 4
 
 
@@ -29,7 +30,7 @@ class DlDesc(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("units", ctypes.c_int32),
                 ("heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("log_len", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("merge_on_step", ctypes.c_int32)]
+                ("merge_on_step", ctypes.c_int32), ("log_form", ctypes.c_int32)]
 
 
 class DlStatePtrs(ctypes.Structure):
@@ -180,11 +181,14 @@ class DecodeState:
     log views ``log_k``/``log_v`` ``[units, H, L, d]`` (input dtype),
     ``log_g`` ``[units, H, L]`` or ``[units, H, L, d]``, ``log_beta``
     ``[units, H, L]`` and ``log_t`` ``[units, H, L(L-1)/2]`` (the packed
-    key-side factors of the delta-rule variants).
+    key-side factors of the delta-rule variants).  With
+    ``log_form=DL_LOG_FACTORS`` (GDN, KDA) ``log_v`` holds the fp32 factors
+    ``a_t`` and there is no ``log_beta`` or ``log_t``.
     """
 
     def __init__(self, variant: int, units: int, heads: int, d: int, log_len: int,
-                 dtype: str = "bf16", device="cuda", stream=None, merge_on_step: bool = False):
+                 dtype: str = "bf16", device="cuda", stream=None, merge_on_step: bool = False,
+                 log_form: int = DL_LOG_WY):
         import torch
 
         self.torch = torch
@@ -192,8 +196,11 @@ class DecodeState:
         self.dtype = dtype
         self.in_torch_dtype = torch.bfloat16 if dtype == "bf16" else torch.float32
         self.merge_on_step = bool(merge_on_step)
+        self.log_form = int(log_form)
+        self.factors = self.log_form == DL_LOG_FACTORS and variant != DL_RWKV6
         self.desc = DlDesc(variant, units, heads, d, d, log_len,
-                           DL_BF16 if dtype == "bf16" else DL_F32, int(self.merge_on_step))
+                           DL_BF16 if dtype == "bf16" else DL_F32, int(self.merge_on_step),
+                           self.log_form)
         nbytes = dl_state_bytes(self.desc)
         if nbytes == 0:
             raise DlError(DL_ERR_INVALID, dl_last_error())
@@ -206,14 +213,15 @@ class DecodeState:
         self.flags = self._view(p.flags, torch.int32, (1,))
         if L > 0:
             self.log_k = self._view(p.log_k, self.in_torch_dtype, (U, H, L, d))
-            self.log_v = self._view(p.log_v, self.in_torch_dtype, (U, H, L, d))
+            self.log_v = self._view(p.log_v, torch.float32 if self.factors else self.in_torch_dtype,
+                                    (U, H, L, d))
             gshape = (U, H, L) if variant == DL_GDN else (U, H, L, d)
             self.log_g = self._view(p.log_g, torch.float32, gshape)
             self.log_beta = (self._view(p.log_beta, torch.float32, (U, H, L))
-                             if variant != DL_RWKV6 else None)
+                             if variant != DL_RWKV6 and not self.factors else None)
             nt = L * (L - 1) // 2
             self.log_t = (self._view(p.log_t, torch.float32, (U, H, nt))
-                          if variant != DL_RWKV6 and nt > 0 else None)
+                          if variant != DL_RWKV6 and nt > 0 and not self.factors else None)
 
     def _view(self, ptr, dtype, shape):
         torch = self.torch

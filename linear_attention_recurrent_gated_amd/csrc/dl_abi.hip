@@ -56,6 +56,8 @@ dl_status check_desc(const dl_desc *d) {
         return fail(DL_ERR_INVALID, "log_len must be >= 0, got %d", d->log_len);
     if (d->merge_on_step != 0 && d->merge_on_step != 1)
         return fail(DL_ERR_INVALID, "merge_on_step must be 0 or 1, got %d", d->merge_on_step);
+    if (d->log_form != DL_LOG_WY && d->log_form != DL_LOG_FACTORS)
+        return fail(DL_ERR_INVALID, "unknown log_form %d", d->log_form);
     if (d->d_k != d->d_v)
         return fail(DL_ERR_UNSUPPORTED, "d_k (%d) != d_v (%d) is not built", d->d_k, d->d_v);
     if (d->d_k != 64 && d->d_k != 128)
@@ -68,12 +70,17 @@ dl_status check_desc(const dl_desc *d) {
     return DL_OK;
 }
 
+// The additive-factor log applies to the delta-rule variants; RWKV6's log
+// has that form already.
+bool factors_form(const dl_desc &d) { return d.log_form == DL_LOG_FACTORS && d.variant != DL_RWKV6; }
+
 Layout layout_of(const dl_desc &d) {
     Layout l;
     const size_t pairs = (size_t)d.units * d.heads;
     const size_t es = d.in_dtype == DL_BF16 ? 2 : 4;
     const size_t L = d.log_len;
     const size_t gch = d.variant == DL_GDN ? 1 : d.d_k;
+    const bool af = factors_form(d);
     size_t off = 0;
     l.off_flags = off;
     off = align256(off + 256);
@@ -84,13 +91,13 @@ Layout layout_of(const dl_desc &d) {
     l.off_k = off;
     off = align256(off + pairs * L * d.d_k * es);
     l.off_v = off;
-    off = align256(off + pairs * L * d.d_v * es);
+    off = align256(off + pairs * L * d.d_v * (af ? 4 : es));
     l.off_g = off;
     off = align256(off + pairs * L * gch * 4);
     l.off_b = off;
-    off = align256(off + (d.variant == DL_RWKV6 ? 0 : pairs * L * 4));
+    off = align256(off + ((d.variant == DL_RWKV6 || af) ? 0 : pairs * L * 4));
     l.off_t = off;
-    off = align256(off + pairs * (size_t)dl::packed_t_len(d.variant, d.log_len) * 4);
+    off = align256(off + (af ? 0 : pairs * (size_t)dl::packed_t_len(d.variant, d.log_len) * 4));
     l.total = off;
     return l;
 }
@@ -140,15 +147,17 @@ dl_status check_lds(const dl_state *st) {
     const int es = st->desc.in_dtype == DL_BF16 ? 2 : 4;
     const dl::StepPlan lp = dl::step_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len,
                                           st->desc.merge_on_step != 0);
-    if (lp.bytes <= 65536)
+    const int bytes = st->p.af ? dl::af_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len).bytes
+                               : lp.bytes;
+    if (bytes <= 65536)
         return DL_OK;
     int dev = 0, max_lds = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
         return fail(DL_ERR_LAUNCH, "cannot query the device's LDS size");
-    if (lp.bytes > max_lds)
+    if (bytes > max_lds)
         return fail(DL_ERR_UNSUPPORTED, "log of %d entries needs %d bytes of LDS (device limit %d)",
-                    st->desc.log_len, lp.bytes, max_lds);
+                    st->desc.log_len, bytes, max_lds);
     return DL_OK;
 }
 
@@ -208,6 +217,7 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.dtype = desc->in_dtype;
     p.flags = reinterpret_cast<int *>(m + l.off_flags);
     p.fuse = desc->merge_on_step;
+    p.af = factors_form(*desc) ? 1 : 0;
     // stream the state when the base is larger than MI355X's 256 MiB Infinity
     // Cache: such a state set cannot stay resident between calls
     p.stream = (size_t)desc->units * desc->heads * desc->d_v * desc->d_k * 4 > ((size_t)256 << 20);
@@ -217,9 +227,10 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.log_k = has_log ? m + l.off_k : nullptr;
     p.log_v = has_log ? m + l.off_v : nullptr;
     p.log_g = has_log ? reinterpret_cast<float *>(m + l.off_g) : nullptr;
-    p.log_beta = (has_log && desc->variant != DL_RWKV6) ? reinterpret_cast<float *>(m + l.off_b)
-                                                        : nullptr;
-    p.log_t = dl::packed_t_len(desc->variant, desc->log_len) > 0
+    p.log_beta = (has_log && desc->variant != DL_RWKV6 && !p.af)
+                     ? reinterpret_cast<float *>(m + l.off_b)
+                     : nullptr;
+    p.log_t = (!p.af && dl::packed_t_len(desc->variant, desc->log_len) > 0)
                   ? reinterpret_cast<float *>(m + l.off_t)
                   : nullptr;
     const hipError_t e = dl::launch_zero(dev_mem, l.total,
@@ -277,8 +288,10 @@ dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx
         return s;
     if (rows == 0)
         return ok();
-    return launched(st, dl::launch_log_step(st->p, rows, slot_idx, q, k, v, g, beta, o,
-                                            launch_of(st, stream)),
+    const dl::Launch ln = launch_of(st, stream);
+    return launched(st,
+                    st->p.af ? dl::launch_af_step(st->p, rows, slot_idx, q, k, v, g, beta, o, ln)
+                             : dl::launch_log_step(st->p, rows, slot_idx, q, k, v, g, beta, o, ln),
                     "log step launch");
 }
 
@@ -292,8 +305,9 @@ static dl_status merge_common(dl_state *st, int32_t rows, const int32_t *slot_id
     if (st->desc.log_len < 1 || rows == 0)
         return ok();
     const dl::Launch ln = launch_of(st, stream);
-    const hipError_t e = wy ? dl::launch_merge_wy(st->p, rows, slot_idx, mode, ln)
-                            : dl::launch_merge_replay(st->p, rows, slot_idx, mode, ln);
+    const hipError_t e = st->p.af ? dl::launch_af_merge(st->p, rows, slot_idx, mode, ln)
+                         : wy     ? dl::launch_merge_wy(st->p, rows, slot_idx, mode, ln)
+                                  : dl::launch_merge_replay(st->p, rows, slot_idx, mode, ln);
     return launched(st, e, "merge launch");
 }
 
@@ -321,7 +335,10 @@ dl_status dl_readout(dl_state *st, int32_t rows, const int32_t *slot_idx, const 
         return s;
     if (rows == 0)
         return ok();
-    return launched(st, dl::launch_readout(st->p, rows, slot_idx, q, o, launch_of(st, stream)),
+    const dl::Launch ln = launch_of(st, stream);
+    return launched(st,
+                    st->p.af ? dl::launch_af_readout(st->p, rows, slot_idx, q, o, ln)
+                             : dl::launch_readout(st->p, rows, slot_idx, q, o, ln),
                     "readout launch");
 }
 
@@ -371,12 +388,14 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
     const double es = d.in_dtype == DL_BF16 ? 2.0 : 4.0;
     const double dk = d.d_k, dv = d.d_v;
     const double St = 4.0 * dv * dk;
+    const bool af = factors_form(d);
     const double gb = d.variant == DL_GDN ? 4.0 : 4.0 * dk;       // decay bytes per entry
-    const double bb = d.variant == DL_RWKV6 ? 0.0 : 4.0;          // beta bytes per entry
+    const double bb = d.variant == DL_RWKV6 ? 0.0 : 4.0;          // beta bytes per input
     const double In = (2.0 * dk + dv) * es + gb + bb;
     const double Out = 4.0 * dv;
-    const double E = (dk + dv) * es + gb + bb;
-    const bool delta = d.variant != DL_RWKV6;
+    // logged entry: key, value (fp32 factor under the additive-factor form), decay, beta
+    const double E = dk * es + dv * (af ? 4.0 : es) + gb + (af ? 0.0 : bb);
+    const bool delta = d.variant != DL_RWKV6 && !af;             // R columns are logged
     const bool fuse = d.merge_on_step != 0;
     int best = 1;
     double best_cost = 0.0, best_bytes = 0.0;
@@ -385,7 +404,8 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
         const double rt = delta ? 4.0 * ((L - 1.0) * (L - 2.0) / 6.0 + c) : 0.0;
         double bytes = St + c * E + E + In + Out + 8.0 + rt;
         bytes += fuse ? St / L : (2.0 * St + L * E + 8.0) / L;
-        const int lds = dl::step_plan(d.variant, d.d_k, (int)es, L, fuse).bytes;
+        const int lds = af ? dl::af_plan(d.variant, d.d_k, (int)es, L).bytes
+                           : dl::step_plan(d.variant, d.d_k, (int)es, L, fuse).bytes;
         const int wgs = std::min(4, (160 * 1024) / std::max(lds, 1));
         const double cost = bytes * 4.0 / std::max(wgs, 1);
         if (L == 1 || cost < best_cost) {

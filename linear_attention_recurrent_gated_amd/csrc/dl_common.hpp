@@ -34,6 +34,8 @@ struct Params {
     int *flags;
     int stream;        // 1: state loads and stores carry the nontemporal hint
     int fuse;          // 1: the log step that fills a log merges it
+    int af;            // 1: additive-factor log (delta-rule variants): log_v holds
+                       //    the fp32 factors a_j, no betas, no R
 };
 
 template <int D>
@@ -206,11 +208,39 @@ struct StepPlan {
     int bytes;
 };
 
+// LDS carve-up of the additive-factor step, readout and merge kernels.
+struct AfPlan {
+    int off_k;     // staged keys, rows of D elements in the input dtype
+    int off_a;     // staged factors a_j, rows of D floats
+    int off_lam;   // staged cumulative log-decays, rows of D floats (per-key
+                   // decays); a merge overwrites rows j < c with k_j D(j, c)
+    int off_r, off_u, off_f;          // per-entry r_j, u_j, (GDN) D(j, n); 64 floats each
+    int off_s;     // GDN: Lam of the newest entry
+    int off_qe, off_ke;               // E q and E k, D floats each
+    int bytes;
+};
+
+__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+__host__ __device__ inline AfPlan af_plan(int variant, int D, int esize, int L) {
+    AfPlan p;
+    p.off_k = 0;
+    p.off_a = round_up(L * D * esize, 1024);
+    p.off_lam = p.off_a + round_up(L * D * 4, 1024);
+    p.off_r = p.off_lam + (variant == DL_GDN ? 0 : round_up(L * D * 4, 1024));
+    p.off_u = p.off_r + 256;
+    p.off_f = p.off_u + 256;
+    p.off_s = p.off_f + 256;
+    p.off_qe = p.off_s + 16;
+    p.off_ke = p.off_qe + D * 4;
+    p.bytes = p.off_ke + D * 4;
+    return p;
+}
+
 __host__ __device__ inline int packed_t_len(int variant, int L) {
     return variant == DL_RWKV6 ? 0 : L * (L - 1) / 2;
 }
 
-__host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
 __host__ __device__ inline StepPlan step_plan(int variant, int D, int esize, int L, bool fuse) {
     StepPlan p;
@@ -337,6 +367,28 @@ __device__ __forceinline__ void reject_row(const Params &P, float *orow, int D, 
         atomicOr(P.flags, flag);
 }
 
+// The (unit, head) pair a merge workgroup owns and its log fill; false when
+// there is nothing to merge (empty log, or not full under DL_MERGE_FULL) or
+// the slot index is out of range (flagged).
+__device__ __forceinline__ bool resolve_merge_pair(const Params &P, const int *slot_idx, int mode,
+                                                   size_t &pair, int &n) {
+    const int H = P.heads;
+    const int pr = blockIdx.x;
+    const int r = pr / H, h = pr - r * H;
+    const int unit = slot_idx ? slot_idx[r] : r;
+    if (unit < 0 || unit >= P.units) {
+        reject_row(P, nullptr, P.D, DL_FLAG_BAD_SLOT);
+        return false;
+    }
+    pair = (size_t)unit * H + h;
+    n = P.fill[pair];
+    if (n <= 0 || n > P.L)
+        return false;
+    if (mode == DL_MERGE_FULL && n != P.L)
+        return false;
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // staging of logged entries into LDS (keys in input dtype, per-entry decays
 // alpha_j, betas; values optional).  Entries j0..j0+n-1 of `pair` go to LDS rows 0..n-1.
@@ -411,6 +463,14 @@ hipError_t launch_readout(const Params &P, int rows, const int *slot_idx, const 
 hipError_t launch_merge_replay(const Params &P, int rows, const int *slot_idx, int mode,
                                const Launch &ln);
 hipError_t launch_merge_wy(const Params &P, int rows, const int *slot_idx, int mode,
+                           const Launch &ln);
+// additive-factor log (dl_step_af.hip)
+hipError_t launch_af_step(const Params &P, int rows, const int *slot_idx, const void *q,
+                          const void *k, const void *v, const float *g, const float *beta,
+                          float *o, const Launch &ln);
+hipError_t launch_af_readout(const Params &P, int rows, const int *slot_idx, const void *q,
+                             float *o, const Launch &ln);
+hipError_t launch_af_merge(const Params &P, int rows, const int *slot_idx, int mode,
                            const Launch &ln);
 
 }  // namespace dl

@@ -32,25 +32,6 @@
 namespace dl {
 
 
-__device__ __forceinline__ bool resolve_merge_pair(const Params &P, const int *slot_idx, int mode,
-                                                   size_t &pair, int &n) {
-    const int H = P.heads;
-    const int pr = blockIdx.x;
-    const int r = pr / H, h = pr - r * H;
-    const int unit = slot_idx ? slot_idx[r] : r;
-    if (unit < 0 || unit >= P.units) {
-        reject_row(P, nullptr, P.D, DL_FLAG_BAD_SLOT);
-        return false;
-    }
-    pair = (size_t)unit * H + h;
-    n = P.fill[pair];
-    if (n <= 0 || n > P.L)
-        return false;
-    if (mode == DL_MERGE_FULL && n != P.L)
-        return false;
-    return true;
-}
-
 // ---------------------------------------------------------------------------
 // replay merge (VALU)
 // ---------------------------------------------------------------------------

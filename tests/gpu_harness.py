@@ -42,10 +42,12 @@ class Case:
 def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
              steps: int | None = None, pairs=None, merge_every_step: bool | None = None,
              run_oracle: bool = True, threads: int | None = None, on_step=None) -> Case:
-    """Run ``paths`` (subset of "eager", "log", "log-replay", "log-fused") over the workload.
+    """Run ``paths`` (subset of "eager", "log", "log-replay", "log-fused",
+    "af", "af-fused") over the workload.
 
     "log" merges a full log with the WY merge after the step that fills it,
-    "log-replay" with the replay merge, "log-fused" inside that step.
+    "log-replay" with the replay merge, "log-fused" inside that step; "af"
+    and "af-fused" are the same two schedules with the additive-factor log.
 
     ``pairs``: selected flat pair indices (unit_total * H + head) to record;
     None records all.  ``on_step(tau, states)`` is called after each step.
@@ -66,7 +68,8 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
         per_layer = []
         for l in range(layers):
             st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype,
-                               merge_on_step=(path == "log-fused"))
+                               merge_on_step=path.endswith("-fused"),
+                               log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY)
             st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
             per_layer.append(st)
         states[path] = per_layer

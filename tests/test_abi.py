@@ -41,22 +41,24 @@ def _align(x):
     return (x + 255) // 256 * 256
 
 
-def _expected_bytes(variant, units, heads, d, L, es):
+def _expected_bytes(variant, units, heads, d, L, es, form=B.DL_LOG_WY):
     pairs = units * heads
+    af = form == B.DL_LOG_FACTORS and variant != B.DL_RWKV6
     total = _align(256) + _align(pairs * 4) + _align(pairs * d * d * 4)
-    total += _align(pairs * L * d * es) * 2
+    total += _align(pairs * L * d * es) + _align(pairs * L * d * (4 if af else es))
     total += _align(pairs * L * (1 if variant == B.DL_GDN else d) * 4)
-    total += _align(0 if variant == B.DL_RWKV6 else pairs * L * 4)
-    total += _align(0 if variant == B.DL_RWKV6 else pairs * (L * (L - 1) // 2) * 4)
+    total += _align(0 if variant == B.DL_RWKV6 or af else pairs * L * 4)
+    total += _align(0 if variant == B.DL_RWKV6 or af else pairs * (L * (L - 1) // 2) * 4)
     return total
 
 
+@pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS])
 @pytest.mark.parametrize("variant", [B.DL_GDN, B.DL_KDA, B.DL_RWKV6])
 @pytest.mark.parametrize("d,L,dt,es", [(128, 16, B.DL_BF16, 2), (64, 32, B.DL_F32, 4),
                                        (128, 0, B.DL_BF16, 2), (64, 64, B.DL_BF16, 2)])
-def test_state_bytes(variant, d, L, dt, es):
-    desc = B.DlDesc(variant, 7, 3, d, d, L, dt)
-    assert B.dl_state_bytes(desc) == _expected_bytes(variant, 7, 3, d, L, es)
+def test_state_bytes(variant, d, L, dt, es, form):
+    desc = B.DlDesc(variant, 7, 3, d, d, L, dt, 0, form)
+    assert B.dl_state_bytes(desc) == _expected_bytes(variant, 7, 3, d, L, es, form)
 
 
 def test_state_bytes_full_size_configs():
@@ -77,6 +79,7 @@ def test_state_bytes_full_size_configs():
     ((0, 4, 2, 96, 96, 8, B.DL_BF16), B.DL_ERR_UNSUPPORTED),    # d not built
     ((0, 4, 2, 128, 128, 65, B.DL_BF16), B.DL_ERR_UNSUPPORTED), # L too long
     ((0, 4, 2, 128, 128, 8, B.DL_BF16, 2), B.DL_ERR_INVALID),   # merge_on_step not 0 / 1
+    ((0, 4, 2, 128, 128, 8, B.DL_BF16, 0, 2), B.DL_ERR_INVALID),  # unknown log form
 ])
 def test_bad_descriptors(lib, fields, code):
     desc = B.DlDesc(*fields)
@@ -117,19 +120,22 @@ def test_null_handle_is_rejected(lib):
 @pytest.mark.parametrize("variant,d,dt,fuse", [(B.DL_GDN, 128, B.DL_BF16, 1), (B.DL_KDA, 128, B.DL_BF16, 1),
                                                (B.DL_KDA, 128, B.DL_BF16, 0), (B.DL_RWKV6, 64, B.DL_BF16, 0),
                                                (B.DL_GDN, 64, B.DL_F32, 0)])
-def test_suggest_log_len(lib, variant, d, dt, fuse):
+@pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS])
+def test_suggest_log_len(lib, variant, d, dt, fuse, form):
     """The suggested L is the argmin of the documented traffic model, and its
     modeled bytes undercut both extremes (merge every step, longest log)."""
-    desc = B.DlDesc(variant, 1, 1, d, d, 0, dt, fuse)
+    desc = B.DlDesc(variant, 1, 1, d, d, 0, dt, fuse, form)
     L, b = B.dl_suggest_log_len(desc)
     assert 1 < L < 64
     es = 2 if dt == B.DL_BF16 else 4
+    af = form == B.DL_LOG_FACTORS and variant != B.DL_RWKV6
     St, g, bb = 4 * d * d, (4 if variant == B.DL_GDN else 4 * d), (0 if variant == B.DL_RWKV6 else 4)
-    In, Out, E = 3 * d * es + g + bb, 4 * d, 2 * d * es + g + bb
+    In, Out = 3 * d * es + g + bb, 4 * d
+    E = d * es + d * (4 if af else es) + g + (0 if af else bb)
 
     def model(L):
         c = (L - 1) / 2
-        rt = 4 * ((L - 1) * (L - 2) / 6 + c) if variant != B.DL_RWKV6 else 0
+        rt = 4 * ((L - 1) * (L - 2) / 6 + c) if variant != B.DL_RWKV6 and not af else 0
         x = St + c * E + E + In + Out + 8 + rt
         return x + (St / L if fuse else (2 * St + L * E + 8) / L)
 

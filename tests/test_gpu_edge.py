@@ -68,17 +68,72 @@ def test_schedule_and_payload_bit_exact(wl, L, path):
     run_case(wl, L, (path,), merge_every_step=True, run_oracle=False, on_step=on_step)
 
 
+@pytest.mark.parametrize("wl,L", [
+    (W.GDN_LARGE.scaled(batch=5, layers=1, heads=2, steps=14), 4),
+    (W.KDA_SWEEP.scaled(batch=3, heads=2, steps=11, ragged=True), 3),
+    (W.GDN_HYBRID.scaled(d_k=64, d_v=64, dtype="f32", batch=2, heads=3, steps=10), 4),
+])
+@pytest.mark.parametrize("path", ["af", "af-fused"])
+def test_factor_log_payload(wl, L, path):
+    """Additive-factor log after every step: fill == (tokens so far) mod L,
+    the slot written holds a bit copy of k, the decay accumulated through it
+    (fp32, entry order), and the factor a_t = beta (v - S_{t-1}(alpha k))
+    within the parity tolerance of the oracle's factor."""
+    first = W.first_active_step(wl, L)
+    H, d = wl.heads, wl.d_k
+    P = wl.batch * H
+    S0 = W.initial_state(wl).reshape(P, d, d)
+    t_start = np.repeat(first, H)
+    hist = []
+    log(f"case factor payload {wl.name} L={L} {path}")
+
+    def on_step(tau, states):
+        st = states[path][0]
+        s = W.draw_step(wl, tau)
+        hist.append(s)
+        if tau > 0:
+            stack = lambda f: np.stack([f(x) for x in hist[:-1]])
+            _, S_prev = oracle.run(wl.variant, stack(lambda x: x.q_f32.reshape(P, d)),
+                                   stack(lambda x: x.k_f32.reshape(P, d)),
+                                   stack(lambda x: x.v_f32.reshape(P, d)),
+                                   stack(lambda x: x.g.reshape(P, -1) if wl.channel_decay else x.g.reshape(P)),
+                                   stack(lambda x: x.beta.reshape(P)), S0, t_start)
+        else:
+            S_prev = S0.astype(np.float64)
+        a_ref = oracle.additive_factor(wl.variant, S_prev, s.k_f32.reshape(P, d), s.v_f32.reshape(P, d),
+                                       s.g.reshape(P, -1) if wl.channel_decay else s.g.reshape(P),
+                                       s.beta.reshape(P)).reshape(wl.batch, H, d)
+        fill = st.fill.cpu().numpy()
+        for b in range(wl.batch):
+            m = tau - first[b] + 1
+            assert np.all(fill[b] == max(m, 0) % L), (tau, b, fill[b])
+            if m <= 0:
+                continue
+            slot = (m - 1) % L
+            assert np.array_equal(_bits(st.log_k[b, :, slot]), _bits(to_torch(s.k[b], wl.dtype)))
+            lam = np.zeros_like(s.g[b])
+            for tp in range(tau - slot, tau + 1):
+                lam = (lam + W.draw_step(wl, tp).g[b]).astype(np.float32)
+            assert np.array_equal(st.log_g[b, :, slot].cpu().numpy(), lam)
+            a = st.log_v[b, :, slot].double().cpu().numpy()
+            e = per_pair_error(a, a_ref[b])
+            assert e.max() <= TOL, (tau, b, e.max())
+
+    run_case(wl, L, (path,), merge_every_step=True, run_oracle=False, on_step=on_step)
+
+
+@pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS], ids=["wy", "factors"])
 @pytest.mark.parametrize("wl", [W.GDN_HYBRID.scaled(batch=2, heads=3, steps=20),
                                 W.KDA_SWEEP.scaled(batch=2, heads=3, steps=20),
                                 W.RWKV6_ADD.scaled(batch=2, heads=3, steps=20)],
                          ids=["gdn", "kda", "rwkv6"])
-def test_readout_matches_oracle(wl):
+def test_readout_matches_oracle(wl, form):
     """dl_readout returns S_t q for a fresh q, mid-log and after merges, and changes nothing."""
     L = 6
     H, d = wl.heads, wl.d_k
     P = wl.batch * H
-    log(f"case readout {wl.name}")
-    st = B.DecodeState(wl.variant, wl.batch, H, d, L, wl.dtype)
+    log(f"case readout {wl.name} form={form}")
+    st = B.DecodeState(wl.variant, wl.batch, H, d, L, wl.dtype, log_form=form)
     eg = B.DecodeState(wl.variant, wl.batch, H, d, 0, wl.dtype)
     S0 = W.initial_state(wl)
     st.base.copy_(torch.from_numpy(S0))
@@ -115,10 +170,11 @@ def test_readout_matches_oracle(wl):
     assert st.check() == 0 and eg.check() == 0
 
 
-def test_device_flags():
+@pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS], ids=["wy", "factors"])
+def test_device_flags(form):
     wl = W.GDN_HYBRID.scaled(batch=2, heads=2, steps=4)
     H, d = wl.heads, wl.d_k
-    st = B.DecodeState(wl.variant, 2, H, d, 2, wl.dtype)
+    st = B.DecodeState(wl.variant, 2, H, d, 2, wl.dtype, log_form=form)
     _, args = _inputs(wl, 0)
     st.step_log(*args)
     st.step_log(*args)
@@ -140,12 +196,13 @@ def test_device_flags():
     st.close()
 
 
-def test_permuted_slots_match_identity():
+@pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS], ids=["wy", "factors"])
+def test_permuted_slots_match_identity(form):
     """Rows map to units through slot_idx in any order."""
     wl = W.KDA_SWEEP.scaled(batch=4, heads=2, steps=9)
     H, d, L = wl.heads, wl.d_k, 4
-    a = B.DecodeState(wl.variant, 4, H, d, L, wl.dtype)
-    b = B.DecodeState(wl.variant, 4, H, d, L, wl.dtype)
+    a = B.DecodeState(wl.variant, 4, H, d, L, wl.dtype, log_form=form)
+    b = B.DecodeState(wl.variant, 4, H, d, L, wl.dtype, log_form=form)
     perm = np.array([2, 0, 3, 1])
     slot = torch.from_numpy(perm.astype(np.int32)).cuda()
     for tau in range(wl.steps):

@@ -41,5 +41,5 @@ def test_full_shape_parity(wl, L, steps):
     T = wl.prefix_steps(L) + steps
     pairs = _sample(wl)
     log(f"case full-shape {wl.name} L={L} T={T} sampled pairs={len(pairs)}")
-    case = run_case(wl, L, ("eager", "log", "log-fused"), steps=T, pairs=pairs)
+    case = run_case(wl, L, ("eager", "log", "log-fused", "af", "af-fused"), steps=T, pairs=pairs)
     assert_parity(case, label=f"{wl.name} L={L}")

@@ -17,7 +17,7 @@ from gpu_harness import assert_parity, log, run_case
 
 pytestmark = pytest.mark.gpu
 
-PATHS = ("eager", "log", "log-replay", "log-fused")
+PATHS = ("eager", "log", "log-replay", "log-fused", "af", "af-fused")
 
 
 def test_tiny_gdn_full_config():

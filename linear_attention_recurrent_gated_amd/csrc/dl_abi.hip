@@ -147,8 +147,7 @@ dl_status check_lds(const dl_state *st) {
     const int es = st->desc.in_dtype == DL_BF16 ? 2 : 4;
     const dl::StepPlan lp = dl::step_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len,
                                           st->desc.merge_on_step != 0);
-    const int bytes = st->p.af ? dl::af_plan(st->desc.variant, st->desc.d_k, es, st->desc.log_len).bytes
-                               : lp.bytes;
+    const int bytes = st->p.af ? dl::af_plan(st->desc.d_k, st->desc.log_len, true).bytes : lp.bytes;
     if (bytes <= 65536)
         return DL_OK;
     int dev = 0, max_lds = 0;
@@ -404,7 +403,7 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
         const double rt = delta ? 4.0 * ((L - 1.0) * (L - 2.0) / 6.0 + c) : 0.0;
         double bytes = St + c * E + E + In + Out + 8.0 + rt;
         bytes += fuse ? St / L : (2.0 * St + L * E + 8.0) / L;
-        const int lds = af ? dl::af_plan(d.variant, d.d_k, (int)es, L).bytes
+        const int lds = af ? dl::af_plan(d.d_k, L, fuse).bytes
                            : dl::step_plan(d.variant, d.d_k, (int)es, L, fuse).bytes;
         const int wgs = std::min(4, (160 * 1024) / std::max(lds, 1));
         const double cost = bytes * 4.0 / std::max(wgs, 1);

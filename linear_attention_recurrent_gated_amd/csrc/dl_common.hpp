@@ -208,32 +208,35 @@ struct StepPlan {
     int bytes;
 };
 
-// LDS carve-up of the additive-factor step, readout and merge kernels.
+// LDS carve-up of the additive-factor step, readout and merge kernels.  Only
+// the factors a_j are staged for every step: each logged key and decay is
+// used by one lane of the step, which loads it straight from the log.
 struct AfPlan {
-    int off_k;     // staged keys, rows of D elements in the input dtype
     int off_a;     // staged factors a_j, rows of D floats
-    int off_lam;   // staged cumulative log-decays, rows of D floats (per-key
-                   // decays); a merge overwrites rows j < c with k_j D(j, c)
-    int off_r, off_u, off_f;          // per-entry r_j, u_j, (GDN) D(j, n); 64 floats each
+    int off_kd;    // merges only: decayed keys k_j D(j, c), rows of D floats
+    int off_r, off_u, off_f;          // per-entry r_j, u_j, (GDN) D(j, c); 64 floats each
     int off_s;     // GDN: Lam of the newest entry
+    int off_lc;    // per-key decays: Lam of the newest entry, D floats
     int off_qe, off_ke;               // E q and E k, D floats each
+    int off_v;     // the step's value row, D elements (up to 4 bytes each)
     int bytes;
 };
 
 __host__ __device__ inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
 
-__host__ __device__ inline AfPlan af_plan(int variant, int D, int esize, int L) {
+__host__ __device__ inline AfPlan af_plan(int D, int L, bool merges) {
     AfPlan p;
-    p.off_k = 0;
-    p.off_a = round_up(L * D * esize, 1024);
-    p.off_lam = p.off_a + round_up(L * D * 4, 1024);
-    p.off_r = p.off_lam + (variant == DL_GDN ? 0 : round_up(L * D * 4, 1024));
+    p.off_a = 0;
+    p.off_kd = round_up(L * D * 4, 1024);
+    p.off_r = p.off_kd + (merges ? round_up(L * D * 4, 1024) : 0);
     p.off_u = p.off_r + 256;
     p.off_f = p.off_u + 256;
     p.off_s = p.off_f + 256;
-    p.off_qe = p.off_s + 16;
+    p.off_lc = p.off_s + 16;
+    p.off_qe = p.off_lc + D * 4;
     p.off_ke = p.off_qe + D * 4;
-    p.bytes = p.off_ke + D * 4;
+    p.off_v = p.off_ke + D * 4;
+    p.bytes = p.off_v + D * 4;
     return p;
 }
 

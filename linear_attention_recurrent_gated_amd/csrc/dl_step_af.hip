@@ -21,49 +21,77 @@
 //
 // Same workgroup shape as the compact-WY step (dl_step.hip): one workgroup of
 // four waves per (row, head), S0 rows in registers (lane groups of 8, lane s
-// holding the columns 4s + 32m + e), the key side of the log staged in LDS by
-// direct-to-LDS loads and shared by all waves through per-entry scalars.
+// holding the columns 4s + 32m + e).  Each logged key and decay is used by
+// exactly one lane (the dot products above, eight channels per lane), so that
+// lane loads it straight from the log -- the first two passes of entries are
+// in flight with S0 -- and only the factors a_j, which every lane group of a
+// row reads, are staged in LDS (direct-to-LDS loads).
 #include "dl_common.hpp"
 
 namespace dl {
 
-// This wave's share of the staging of entries [0, n): keys, factors and
-// (per-key decays) cumulative log-decays.  Lanes past the last element are
-// masked off.
-template <int V, int D, typename T>
-__device__ __forceinline__ void af_stage(const Params &P, size_t pair, int n, unsigned char *smem,
-                                         const AfPlan &ap, int lane, int wave) {
-    const size_t e0 = pair * P.L;
-    constexpr int CPK = D * (int)sizeof(T) / 16;   // 16-byte chunks per key row
-    constexpr int CPF = D / 4;                     // per fp32 row
-    const int nk = n * CPK, nf = n * CPF;
-    const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_k) + e0 * D);
-    const uint4 *as = reinterpret_cast<const uint4 *>(static_cast<const float *>(P.log_v) + e0 * D);
-    for (int b = 64 * wave; b < nk; b += 256) {
-        const int idx = b + lane;
-        if (idx < nk)
-            load_to_lds<16>(ks + idx, smem + ap.off_k + 16 * b);
-    }
+// This wave's share of the staging of the factors of entries [0, n).  Lanes
+// past the last element are masked off.
+__device__ __forceinline__ void af_stage_factors(const Params &P, size_t pair, int n, int D,
+                                                 unsigned char *smem, const AfPlan &ap, int lane,
+                                                 int wave) {
+    const int nf = n * (D / 4);
+    const uint4 *as = reinterpret_cast<const uint4 *>(static_cast<const float *>(P.log_v) + pair * P.L * D);
     for (int b = 64 * wave; b < nf; b += 256) {
         const int idx = b + lane;
         if (idx < nf)
             load_to_lds<16>(as + idx, smem + ap.off_a + 16 * b);
     }
+}
+
+// Raw key-side data of one logged entry on one lane: eight channels of the
+// key (input dtype) and, for per-key decays, of the cumulative log-decay.
+struct KeyRaw {
+    uint4 k0, k1;
+    float4 l0, l1;
+};
+
+template <int V, int D, typename T>
+__device__ __forceinline__ void load_key_raw(const Params &P, size_t e, int ch0, KeyRaw &rw) {
+    const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_k) + e * D + ch0);
+    rw.k0 = kp[0];
+    if constexpr (sizeof(T) == 4)
+        rw.k1 = kp[1];
     if constexpr (V != GDN) {
-        const uint4 *ls = reinterpret_cast<const uint4 *>(P.log_g + e0 * D);
-        for (int b = 64 * wave; b < nf; b += 256) {
-            const int idx = b + lane;
-            if (idx < nf)
-                load_to_lds<16>(ls + idx, smem + ap.off_lam + 16 * b);
-        }
+        const float4 *lp = reinterpret_cast<const float4 *>(P.log_g + e * D + ch0);
+        rw.l0 = lp[0];
+        rw.l1 = lp[1];
+    }
+}
+
+// Eight input elements kept as loaded (bf16 pairs or floats) until use.
+struct Raw8 {
+    uint4 a, b;
+};
+
+template <typename T>
+__device__ __forceinline__ void load_raw8(const T *p, Raw8 &r) {
+    r.a = reinterpret_cast<const uint4 *>(p)[0];
+    if constexpr (sizeof(T) == 4)
+        r.b = reinterpret_cast<const uint4 *>(p)[1];
+}
+
+template <typename T>
+__device__ __forceinline__ void unpack8(const uint4 &a, const uint4 &b, float *x) {
+    if constexpr (sizeof(T) == 4) {
+        x[0] = __uint_as_float(a.x), x[1] = __uint_as_float(a.y);
+        x[2] = __uint_as_float(a.z), x[3] = __uint_as_float(a.w);
+        x[4] = __uint_as_float(b.x), x[5] = __uint_as_float(b.y);
+        x[6] = __uint_as_float(b.z), x[7] = __uint_as_float(b.w);
+    } else {
+        x[0] = bf16_lo(a.x), x[1] = bf16_hi(a.x), x[2] = bf16_lo(a.y), x[3] = bf16_hi(a.y);
+        x[4] = bf16_lo(a.z), x[5] = bf16_hi(a.z), x[6] = bf16_lo(a.w), x[7] = bf16_hi(a.w);
     }
 }
 
 // S0 <- S0 diag(E_c) + sum_{j < ct} a_j kd_j^T on this wave's rows, then the
-// rows go back to the base.  kd_j = k_j D(j, c): GDN scales the staged key by
-// the per-entry factor; KDA finds rows j < ct - 1 already decayed in the
-// log-decay region (row ct - 1, D = 1, is the key itself).
-template <int V, int D, typename T, bool NT>
+// rows go back to the base; kd_j = k_j D(j, c) is staged in LDS.
+template <int V, int D, bool NT>
 __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int ct,
                                               const unsigned char *smem, const AfPlan &ap,
                                               float4 (&st)[Shape<D>::ITER][Shape<D>::NCH]) {
@@ -71,9 +99,7 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 3, s = lane & 7;
     const float *sa = reinterpret_cast<const float *>(smem + ap.off_a);
-    const float *slam = reinterpret_cast<const float *>(smem + ap.off_lam);
-    const float *sf = reinterpret_cast<const float *>(smem + ap.off_f);
-    const unsigned char *sk = smem + ap.off_k;
+    const float *skd = reinterpret_cast<const float *>(smem + ap.off_kd);
     float ec[SH::FPL];
     if constexpr (V == GDN) {
         const float e = fast_exp(reinterpret_cast<const float *>(smem + ap.off_s)[0]);
@@ -81,9 +107,10 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
         for (int i = 0; i < SH::FPL; ++i)
             ec[i] = e;
     } else {
+        const float *slc = reinterpret_cast<const float *>(smem + ap.off_lc);
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m) {
-            const float4 l = *reinterpret_cast<const float4 *>(slam + (ct - 1) * D + col_of(s, m, 0));
+            const float4 l = *reinterpret_cast<const float4 *>(slc + col_of(s, m, 0));
             ec[4 * m] = fast_exp(l.x), ec[4 * m + 1] = fast_exp(l.y);
             ec[4 * m + 2] = fast_exp(l.z), ec[4 * m + 3] = fast_exp(l.w);
         }
@@ -97,19 +124,9 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
         }
     for (int j = 0; j < ct; ++j) {
         float kd[SH::FPL];
-        if (V == GDN || j == ct - 1) {
-            const float f = (V == GDN) ? sf[j] : 1.f;
 #pragma unroll
-            for (int m = 0; m < SH::NCH; ++m) {
-                const float4 kk = lds_load4<T>(sk + (size_t)j * D * sizeof(T), col_of(s, m, 0));
-                kd[4 * m] = f * kk.x, kd[4 * m + 1] = f * kk.y;
-                kd[4 * m + 2] = f * kk.z, kd[4 * m + 3] = f * kk.w;
-            }
-        } else {
-#pragma unroll
-            for (int m = 0; m < SH::NCH; ++m)
-                f4_to(kd + 4 * m, *reinterpret_cast<const float4 *>(slam + j * D + col_of(s, m, 0)));
-        }
+        for (int m = 0; m < SH::NCH; ++m)
+            f4_to(kd + 4 * m, *reinterpret_cast<const float4 *>(skd + j * D + col_of(s, m, 0)));
 #pragma unroll
         for (int it = 0; it < SH::ITER; ++it) {
             const float aj = sa[j * D + wave * SH::RPW + it * 8 + grp];
@@ -132,11 +149,12 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
 
 // One workgroup per (row, head).  APPEND: the step (append + readout);
 // otherwise a readout of base + log.  FUSE: the step that fills the log
-// also merges it (fill back to 0).  Logs of up to 32 bf16 entries fit four
-// workgroups per CU in LDS; the kernel is then held to the registers of four
-// waves per SIMD as well.
+// also merges it (fill back to 0).  With bf16 inputs and logs of up to 32
+// entries the kernel is held to the registers of four waves per SIMD (four
+// workgroups per CU), except where that spills on the hot path (per-key
+// decays, 32 entries, merge in the step), which runs three.
 template <int V, int D, typename T, bool APPEND, int MV, bool NT, bool FUSE>
-__global__ void __launch_bounds__(256, (MV <= 4 && sizeof(T) == 2) ? 4 : 1)
+__global__ void __launch_bounds__(256, (MV <= 4 && sizeof(T) == 2) ? ((V == KDA && FUSE && MV == 4) ? 3 : 4) : 1)
 af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
                const float *__restrict__ beta, float *__restrict__ o) {
@@ -159,14 +177,14 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     const size_t pair = (size_t)unit * H + h;
     const size_t io = (size_t)pr * D;
     const size_t e0 = pair * L;
-    const AfPlan ap = af_plan(V, D, (int)sizeof(T), L);
-    T *sk = reinterpret_cast<T *>(smem + ap.off_k);
+    const AfPlan ap = af_plan(D, L, FUSE);
     float *sa = reinterpret_cast<float *>(smem + ap.off_a);
-    float *slam = reinterpret_cast<float *>(smem + ap.off_lam);
+    float *skd = reinterpret_cast<float *>(smem + ap.off_kd);
     float *sr = reinterpret_cast<float *>(smem + ap.off_r);
     float *su = reinterpret_cast<float *>(smem + ap.off_u);
     float *sf = reinterpret_cast<float *>(smem + ap.off_f);
     float *ss = reinterpret_cast<float *>(smem + ap.off_s);
+    float *slc = reinterpret_cast<float *>(smem + ap.off_lc);
     float *sqe = reinterpret_cast<float *>(smem + ap.off_qe);
     float *ske = reinterpret_cast<float *>(smem + ap.off_ke);
 
@@ -183,26 +201,49 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
             st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
     const int cg = lane % G, ro = lane / G, ch0 = 8 * cg;
-    float qv[8], kn[8];
-    load8<T>(q + io + ch0, qv);
+    Raw8 qr = {}, kr = {};               // q and k on this lane's channels, as loaded
+    load_raw8<T>(q + io + ch0, qr);
     if constexpr (APPEND)
-        load8<T>(k + io + ch0, kn);
+        load_raw8<T>(k + io + ch0, kr);
     __builtin_amdgcn_sched_barrier(0);
     if (APPEND ? (n >= L || n < 0) : (n > L || n < 0)) {
         reject_row(P, orow, D, DL_FLAG_LOG_FULL);
         return;
     }
 
-    // ---- loads that need n: the new value on this lane's rows, beta, the
-    //      staging, and (wave 0) Lam and the decayed q and k
-    float vc[SH::ITER];
-#pragma unroll
-    for (int it = 0; it < SH::ITER; ++it)
-        vc[it] = APPEND ? Elem<T>::load1(v + io + wave * SH::RPW + it * 8 + grp) : 0.f;
+    // ---- loads that need n: beta, this lane's logged keys (and decays) of
+    //      the first pass(es), the staging of the factors and of the new
+    //      value row, and (wave 0) Lam and the decayed q and k
     const float b_in = APPEND ? beta[pr] : 0.f;
-    if (n > 0)
-        af_stage<V, D, T>(P, pair, n, smem, ap, lane, wave);
+    if constexpr (APPEND) {
+        constexpr int CPV = D * (int)sizeof(T) / 16;
+        if (wave == 0 && lane < CPV)
+            load_to_lds<16>(reinterpret_cast<const uint4 *>(v + io) + lane, smem + ap.off_v);
+    }
     const int ct = APPEND ? n + 1 : n;   // entries the readout sees
+    const int npass = (ct + PASS - 1) / PASS;
+    // logged entry j of pass p on this lane (clamped to the last logged one)
+    auto entry_of = [&](int p) {
+        const int j = PASS * p + RP * wave + ro;
+        return e0 + (j < n ? j : n - 1);
+    };
+    // Every pass gets its own registers (NP passes cover MV * 8 >= L
+    // entries).  Before the barrier: two passes of keys (head-wise decay) or
+    // one pass of keys and decays (per-key decays, twice the data); the rest
+    // right after it, all in flight together.
+    constexpr int NP = (8 * MV + PASS - 1) / PASS;
+    constexpr int EARLY = (V == GDN && NP > 1) ? 2 : 1;
+    KeyRaw pre[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+        pre[p] = KeyRaw{};
+    if (n > 0) {
+#pragma unroll
+        for (int p = 0; p < EARLY; ++p)
+            if (p < npass)
+                load_key_raw<V, D, T>(P, entry_of(p), ch0, pre[p]);
+        af_stage_factors(P, pair, n, D, smem, ap, lane, wave);
+    }
     if (wave == 0) {
         float en[8];                     // E_c on this lane's channels
         if constexpr (V == GDN) {
@@ -233,60 +274,63 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     lc[i] += gn[i];
-                if (ro == 0)
-                    store8<float>(slam + n * D + ch0, lc);
             }
+            if (ro == 0)
+                store8<float>(slc + ch0, lc);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 en[i] = fast_exp(lc[i]);
         }
         if (ro == 0) {
             float t[8];
+            unpack8<T>(qr.a, qr.b, t);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                t[i] = en[i] * qv[i];
+                t[i] *= en[i];
             store8<float>(sqe + ch0, t);
             if constexpr (APPEND) {
+                unpack8<T>(kr.a, kr.b, t);
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
-                    t[i] = en[i] * kn[i];
+                    t[i] *= en[i];
                 store8<float>(ske + ch0, t);
-                store8<T>(sk + n * D + ch0, kn);
             }
         }
     }
-    wait_vm_all();      // this wave's staging (and everything before it) has landed
-    __syncthreads();    // 1: staged entries, the new entry, Lam, E q, E k
+    wait_vm_all();      // this wave's loads and staging have landed
+    __syncthreads();    // 1: staged factors, Lam_c, per-entry factors, E q, E k
 
     const bool merging = FUSE && APPEND && n == L - 1;
-    float lc[8];
-    if constexpr (V != GDN) {
-        if (ct > 0)
-            load8<float>(slam + (ct - 1) * D + ch0, lc);
-        else
+    if (n > 0) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                lc[i] = 0.f;
+        for (int p = EARLY; p < NP; ++p)
+            if (p < npass)
+                load_key_raw<V, D, T>(P, entry_of(p), ch0, pre[p]);
     }
+    float lc[8];
+    if constexpr (V != GDN)
+        load8<float>(slc + ch0, lc);
 
-    // ---- r_j = (k_j D(j, c)) . q and u_j = (k_j D(j, c)) . k for this
-    //      wave's entries of each pass; a merging step keeps k_j D(j, c)
-    //      (per-key decays) in place of Lam_j for the merge
-    const int npass = (ct + PASS - 1) / PASS;
-    for (int p = 0; p < npass; ++p) {
+    // ---- r_j = (k_j D(j, c)) . q and u_j = (k_j D(j, c)) . k for this lane's
+    //      entry of each pass (the new entry n is this step's k, D = 1); a
+    //      merging step also keeps k_j D(j, c) for the merge
+    auto process = [&](int p, const KeyRaw &rw) {
         const int j = PASS * p + RP * wave + ro;
-        const int jc = j < ct ? j : ct - 1;
-        float kd[8];
-        load8<T>(sk + jc * D + ch0, kd);
+        float kd[8], qv[8], kn[8];
+        unpack8<T>(rw.k0, rw.k1, kd);
+        unpack8<T>(qr.a, qr.b, qv);
+        if constexpr (APPEND)
+            unpack8<T>(kr.a, kr.b, kn);
         if constexpr (V != GDN) {
-            float lr[8];
-            load8<float>(slam + jc * D + ch0, lr);
+            const float lr[8] = {rw.l0.x, rw.l0.y, rw.l0.z, rw.l0.w, rw.l1.x, rw.l1.y, rw.l1.z, rw.l1.w};
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 kd[i] *= fast_exp(lc[i] - lr[i]);
-            if (FUSE && merging && j < n)
-                store8<float>(slam + j * D + ch0, kd);
         }
+        if (APPEND && j == n)
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                kd[i] = kn[i];
         float ar = 0.f, au = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -297,13 +341,24 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
         ar = group_sum<G>(ar);
         if constexpr (APPEND)
             au = group_sum<G>(au);
-        const float f = (V == GDN) ? sf[jc] : 1.f;
+        const float f = (V == GDN) ? sf[j < ct ? j : ct - 1] : 1.f;
         if (cg == 0 && j < ct) {
             sr[j] = f * ar;
             if constexpr (APPEND)
                 su[j] = f * au;
         }
-    }
+        if (FUSE && merging && j < ct) {
+            if constexpr (V == GDN)
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    kd[i] *= f;
+            store8<float>(skd + j * D + ch0, kd);
+        }
+    };
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+        if (p < npass)
+            process(p, pre[p]);
     __syncthreads();    // 2: r and u of every entry (and the merge's decayed keys)
 
     // ---- per row: x = S0 (E k) + sum u_j a_j, a_n = beta (v - x),
@@ -348,7 +403,8 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
         ao = sum8(ao);
         if constexpr (APPEND) {
             ax = sum8(ax);
-            const float an = b_in * (vc[it] - ax);
+            const float vr = Elem<T>::load1(reinterpret_cast<const T *>(smem + ap.off_v) + row);
+            const float an = b_in * (vr - ax);
             ao += rn * an;
             if (s == 1)
                 alog[row] = an;
@@ -361,23 +417,25 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     if constexpr (APPEND) {
         // the rest of entry n: the key (bit copy) and Lam_n
         if (wave == 0) {
-            constexpr int CPK = D * (int)sizeof(T) / 16;
-            if (lane < CPK)
-                reinterpret_cast<uint4 *>(static_cast<T *>(P.log_k) + (e0 + n) * D)[lane] =
-                    reinterpret_cast<const uint4 *>(sk + n * D)[lane];
+            if (ro == 0) {
+                uint4 *dst = reinterpret_cast<uint4 *>(static_cast<T *>(P.log_k) + (e0 + n) * D + ch0);
+                dst[0] = kr.a;
+                if constexpr (sizeof(T) == 4)
+                    dst[1] = kr.b;
+            }
             if constexpr (V == GDN) {
                 if (lane == 0)
                     P.log_g[e0 + n] = ss[0];
             } else {
                 if (lane < D / 4)
                     reinterpret_cast<float4 *>(P.log_g + (e0 + n) * D)[lane] =
-                        reinterpret_cast<const float4 *>(slam + n * D)[lane];
+                        reinterpret_cast<const float4 *>(slc)[lane];
             }
         }
         if constexpr (FUSE) {
             if (merging) {
                 wave_lds_sync();   // this wave's rows of a_n are in LDS
-                af_merge_rows<V, D, T, NT>(P, pair, ct, smem, ap, st);
+                af_merge_rows<V, D, NT>(P, pair, ct, smem, ap, st);
                 if (tid == 0)
                     P.fill[pair] = 0;
                 return;
@@ -402,7 +460,7 @@ __global__ void __launch_bounds__(256) af_merge_kernel(Params P, const int *__re
         return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 3, s = lane & 7;
-    const AfPlan ap = af_plan(V, D, (int)sizeof(T), P.L);
+    const AfPlan ap = af_plan(D, P.L, true);
     const size_t e0 = pair * P.L;
     const float *Sp = P.base + pair * D * D;
     float4 st[SH::ITER][SH::NCH];
@@ -413,39 +471,52 @@ __global__ void __launch_bounds__(256) af_merge_kernel(Params P, const int *__re
         for (int m = 0; m < SH::NCH; ++m)
             st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
-    af_stage<V, D, T>(P, pair, n, smem, ap, lane, wave);
-    if constexpr (V == GDN) {
-        if (wave == 0) {
+    af_stage_factors(P, pair, n, D, smem, ap, lane, wave);
+    float *sf = reinterpret_cast<float *>(smem + ap.off_f);
+    float *slc = reinterpret_cast<float *>(smem + ap.off_lc);
+    if (wave == 0) {
+        if constexpr (V == GDN) {
             const int jl = lane < n ? lane : n - 1;
             const float lam_j = P.log_g[e0 + jl];
             const float lam_c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_j), n - 1));
             if (lane < n)
-                reinterpret_cast<float *>(smem + ap.off_f)[lane] = fast_exp(lam_c - lam_j);
+                sf[lane] = fast_exp(lam_c - lam_j);
             if (lane == 0)
                 reinterpret_cast<float *>(smem + ap.off_s)[0] = lam_c;
+        } else {
+            if (lane < D / 4)
+                reinterpret_cast<float4 *>(slc)[lane] =
+                    reinterpret_cast<const float4 *>(P.log_g + (e0 + n - 1) * D)[lane];
         }
     }
     wait_vm_all();
     __syncthreads();
-    if constexpr (V != GDN) {
-        // decayed keys k_j D(j, c) in place of Lam_j, j < n - 1
+    // decayed keys k_j D(j, c), eight channels per thread and step
+    {
         constexpr int CPR = D / 8;
-        const T *sk = reinterpret_cast<const T *>(smem + ap.off_k);
-        float *slam = reinterpret_cast<float *>(smem + ap.off_lam);
-        for (int idx = tid; idx < (n - 1) * CPR; idx += 256) {
+        float *skd = reinterpret_cast<float *>(smem + ap.off_kd);
+        for (int idx = tid; idx < n * CPR; idx += 256) {
             const int j = idx / CPR, c = 8 * (idx - j * CPR);
-            float kr[8], lr[8], lc[8];
-            load8<T>(sk + j * D + c, kr);
-            load8<float>(slam + j * D + c, lr);
-            load8<float>(slam + (n - 1) * D + c, lc);
+            float kr[8];
+            load8<T>(static_cast<const T *>(P.log_k) + (e0 + j) * D + c, kr);
+            if constexpr (V == GDN) {
+                const float f = sf[j];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                kr[i] *= fast_exp(lc[i] - lr[i]);
-            store8<float>(slam + j * D + c, kr);
+                for (int i = 0; i < 8; ++i)
+                    kr[i] *= f;
+            } else {
+                float lr[8], lcv[8];
+                load8<float>(P.log_g + (e0 + j) * D + c, lr);
+                load8<float>(slc + c, lcv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    kr[i] *= fast_exp(lcv[i] - lr[i]);
+            }
+            store8<float>(skd + j * D + c, kr);
         }
-        __syncthreads();
     }
-    af_merge_rows<V, D, T, NT>(P, pair, n, smem, ap, st);
+    __syncthreads();
+    af_merge_rows<V, D, NT>(P, pair, n, smem, ap, st);
     if (tid == 0)
         P.fill[pair] = 0;
 }
@@ -478,7 +549,7 @@ static void af_launch(const Params &P, int rows, const int *slot_idx, const void
                       const void *k, const void *v, const float *g, const float *beta, float *o,
                       const Launch &ln) {
     const bool fuse = APPEND && P.fuse;
-    const AfPlan ap = af_plan(V, D, (int)sizeof(T), P.L);
+    const AfPlan ap = af_plan(D, P.L, fuse);
     const dim3 grid(rows * P.heads), block(256);
 #define DL_AF_LAUNCH(NTV, FV)                                                                          \
     hipExtLaunchKernelGGL((af_step_kernel<V, D, T, APPEND, MV, NTV, FV>), grid, block, ap.bytes,       \
@@ -526,7 +597,7 @@ static hipError_t af_readout_t(const Params &P, int rows, const int *slot_idx, c
 template <int V, int D, typename T>
 static hipError_t af_merge_t(const Params &P, int rows, const int *slot_idx, int mode,
                              const Launch &ln) {
-    const AfPlan ap = af_plan(V, D, (int)sizeof(T), P.L);
+    const AfPlan ap = af_plan(D, P.L, true);
     if (P.stream)
         hipExtLaunchKernelGGL((af_merge_kernel<V, D, T, true>), dim3(rows * P.heads), dim3(256), ap.bytes,
                               ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode);

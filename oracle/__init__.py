@@ -29,7 +29,7 @@ import numpy as np
 
 from .build import LIB_PATH, build_oracle, needs_build
 
-GDN, KDA, RWKV6 = 0, 1, 2
+GDN, KDA, RWKV6, GDN2 = 0, 1, 2, 3
 
 _libs: dict = {}
 
@@ -72,7 +72,8 @@ def run(variant: int, q, k, v, g, beta=None, S0=None, t_start=None, threads: int
 
     Shapes: ``q, k`` ``[T, P, d_k]``; ``v`` ``[T, P, d_v]``; ``g`` ``[T, P]``
     (head-wise decay) or ``[T, P, d_k]`` (channel-wise); ``beta`` ``[T, P]``
-    (not used by the additive variant); ``S0`` ``[P, d_v, d_k]`` or None for
+    (not used by the additive variant; ``[T, P, d_k + d_v]`` -- erase gate,
+    then write gate -- for the gated form); ``S0`` ``[P, d_v, d_k]`` or None for
     zeros; ``t_start`` ``[P]`` first step each state takes (outputs before it
     are zero).  All float inputs are the exact values the kernels consume.
 
@@ -86,7 +87,9 @@ def run(variant: int, q, k, v, g, beta=None, S0=None, t_start=None, threads: int
         assert g.shape == (T, P)
     else:
         assert g.shape == (T, P, dk)
-    if variant != RWKV6:
+    if variant == GDN2:
+        assert beta is not None and beta.shape == (T, P, dk + dv)
+    elif variant != RWKV6:
         assert beta is not None and beta.shape == (T, P)
     else:
         beta = None
@@ -119,12 +122,14 @@ def additive_factor(variant: int, S_prev, k, v, g, beta=None):
     A step writes ``S_t = S_{t-1} diag(alpha_t) + a_t k_t^T`` with
     ``alpha_t = exp(g_t)`` (a scalar for the head-wise decay) and
     ``a_t = beta_t (v_t - S_{t-1} (alpha_t * k_t))`` for the delta-rule
-    operators, ``a_t = v_t`` for the additive one: the factor pair
-    ``(a_t, b_t = k_t)`` that the DeltaLog page's Core Mechanism appends to
-    the log instead of writing the state.
+    operators, ``a_t = w_t * v_t - S_{t-1} (alpha_t * e_t * k_t)`` for the
+    gated form (erase gate ``e_t``, write gate ``w_t``), ``a_t = v_t`` for the
+    additive one: the factor pair ``(a_t, b_t = k_t)`` that the DeltaLog
+    page's Core Mechanism appends to the log instead of writing the state.
 
     Shapes: ``S_prev`` ``[P, d_v, d_k]``; ``k`` ``[P, d_k]``; ``v`` ``[P, d_v]``;
-    ``g`` ``[P]`` or ``[P, d_k]``; ``beta`` ``[P]``.  Returns ``[P, d_v]``.
+    ``g`` ``[P]`` or ``[P, d_k]``; ``beta`` ``[P]`` (gated: ``[P, d_k + d_v]``).
+    Returns ``[P, d_v]``.
     """
     S = np.asarray(S_prev, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -133,8 +138,13 @@ def additive_factor(variant: int, S_prev, k, v, g, beta=None):
         return v.copy()
     g = np.asarray(g, dtype=np.float64)
     alpha = np.exp(g)[:, None] if variant == GDN else np.exp(g)
+    beta = np.asarray(beta, dtype=np.float64)
+    if variant == GDN2:
+        dk = k.shape[1]
+        erase, write = beta[:, :dk], beta[:, dk:]
+        return write * v - np.einsum("pij,pj->pi", S, alpha * erase * k)
     x = np.einsum("pij,pj->pi", S, alpha * k)
-    return np.asarray(beta, dtype=np.float64)[:, None] * (v - x)
+    return beta[:, None] * (v - x)
 
 
 def max_threads() -> int:

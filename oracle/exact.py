@@ -7,7 +7,9 @@ rational), so every result is exact.
 
 Notation: a state ``S`` is a ``d_v x d_k`` list of rows; vectors are lists.
 Variants: 0 = Gated DeltaNet (scalar ``alpha``), 1 = KDA (per-key-channel
-``alpha``), 2 = RWKV6-style additive (per-channel ``w``, no ``beta``).
+``alpha``), 2 = RWKV6-style additive (per-channel ``w``, no ``beta``),
+3 = the gated form (per-key ``alpha``; ``beta`` is a pair ``(e, w)`` of an
+erase gate on the key channels and a write gate on the value channels).
 
 Sources:
 
@@ -32,7 +34,7 @@ from __future__ import annotations
 
 from fractions import Fraction as Fr
 
-GDN, KDA, RWKV6 = 0, 1, 2
+GDN, KDA, RWKV6, GDN2 = 0, 1, 2, 3
 
 
 # ----------------------------------------------------------------------------
@@ -89,17 +91,22 @@ def transform(variant, alpha, beta, k):
     """The right factor ``A_t`` acting on the old state.
 
     GDN ``alpha (I - beta k k^T)``; KDA ``diag(alpha) (I - beta k k^T)``;
-    RWKV6 ``diag(w)``.
+    RWKV6 ``diag(w)``; gated ``diag(alpha) (I - (e * k) k^T)``.
     """
     dk = len(k)
     D = diag(_chan(variant, alpha, dk))
     if variant == RWKV6:
         return D
+    if variant == GDN2:
+        e = [Fr(x) * Fr(kk) for x, kk in zip(beta[0], k)]
+        return matmul(D, madd(eye(dk), outer(e, k), -Fr(1)))
     return matmul(D, madd(eye(dk), outer(k, k), -Fr(beta)))
 
 
 def write_term(variant, beta, k, v):
-    """The additive term: ``beta v k^T`` (RWKV6: ``v k^T``)."""
+    """The additive term: ``beta v k^T`` (RWKV6: ``v k^T``; gated: ``(w * v) k^T``)."""
+    if variant == GDN2:
+        return outer([Fr(w) * Fr(x) for w, x in zip(beta[1], v)], k)
     c = Fr(1) if variant == RWKV6 else Fr(beta)
     return [[c * x for x in row] for row in outer(v, k)]
 
@@ -382,7 +389,8 @@ def af_append(variant, base, log, k, v, alpha, beta):
     page's Core Mechanism.  For a step with ``(k, v, alpha, beta)``:
     ``P_n = P_{n-1} * alpha``, ``b = k`` and ``a = beta (v - x)`` with
     ``x = S_{n-1} (alpha * k) = base (P_n * k) + sum_{j<n} a_j (b_j * P_n / P_j) . k``,
-    read from base and log without materialising ``S_{n-1}`` (RWKV6: ``a = v``).
+    read from base and log without materialising ``S_{n-1}`` (RWKV6: ``a = v``;
+    gated: ``a = w * v - x`` with ``e * k`` in place of ``k`` in ``x``).
     """
     dk = len(k)
     prev = log[-1][2] if log else [Fr(1)] * dk
@@ -391,10 +399,13 @@ def af_append(variant, base, log, k, v, alpha, beta):
     vf = [Fr(x) for x in v]
     if variant == RWKV6:
         return (vf, kf, Pn)
-    x = matvec(base, [p * kk for p, kk in zip(Pn, kf)])
+    rd = [Fr(e) * kk for e, kk in zip(beta[0], kf)] if variant == GDN2 else kf
+    x = matvec(base, [p * kk for p, kk in zip(Pn, rd)])
     for a, b, Pj in log:
-        u = sum((bb * p / pj * kk for bb, p, pj, kk in zip(b, Pn, Pj, kf)), Fr(0))
+        u = sum((bb * p / pj * kk for bb, p, pj, kk in zip(b, Pn, Pj, rd)), Fr(0))
         x = [xi + u * ai for xi, ai in zip(x, a)]
+    if variant == GDN2:
+        return ([Fr(w) * vi - xi for w, vi, xi in zip(beta[1], vf, x)], kf, Pn)
     return ([Fr(beta) * (vi - xi) for vi, xi in zip(vf, x)], kf, Pn)
 
 

@@ -13,6 +13,7 @@
  *   Gated DeltaNet  S_t = alpha_t * S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
  *   KDA             S_t = S_{t-1} diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
  *   RWKV6-style     S_t = S_{t-1} diag(w_t) + v_t k_t^T
+ *   gated (GDN-2)   S_t = S_{t-1} diag(alpha_t) (I - (e_t * k_t) k_t^T) + (w_t * v_t) k_t^T
  *   readout         o_t = S_t q_t
  *
  * with S a d_v x d_k matrix (row = value channel, column = key channel),
@@ -27,6 +28,12 @@
  * deferred (base + log) schedule changes none of this arithmetic (DeltaLog
  * page, Methodology), so the oracle is the plain recurrence.
  *
+ * The gated form follows the Gated DeltaNet-2 abstract: KDA's single scalar
+ * beta is split into a channel-wise erase gate e_t on the key channels
+ * (how much of the stored content along k_t is read out and removed) and a
+ * channel-wise write gate w_t on the value channels (how much of v_t is
+ * committed), and it becomes KDA when both gates are the same scalar.
+ *
  * Every product is written out as the formula's terms: the decayed state,
  * its product with k, the two rank-one terms, then the readout.  Inputs are
  * the exact values the GPU consumes (bf16 or fp32, passed here as float32)
@@ -40,7 +47,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_GDN = 0, ORACLE_KDA = 1, ORACLE_RWKV6 = 2 };
+enum { ORACLE_GDN = 0, ORACLE_KDA = 1, ORACLE_RWKV6 = 2, ORACLE_GDN2 = 3 };
 
 /* S[i][j] *= a  (the scalar head-wise decay) */
 static void scale_all(int dv, int dk, double *S, double a)
@@ -90,6 +97,8 @@ static void run_one(int variant, int64_t pair, int64_t n_pairs, int dk, int dv, 
     double *al = vd + dv;         /* d_k */
     double *Sk = al + dk;         /* d_v */
     double *ot = Sk + dv;         /* d_v */
+    double *ek = ot + dv;         /* d_k */
+    double *wv = ek + dk;         /* d_v */
 
     for (size_t e = 0; e < (size_t)dv * dk; ++e)
         S[e] = S0 ? (double)S0[(size_t)pair * dv * dk + e] : 0.0;
@@ -126,6 +135,20 @@ static void run_one(int variant, int64_t pair, int64_t n_pairs, int dk, int dv, 
             matvec(dv, dk, S, kd, Sk);
             add_outer(dv, dk, S, -b, Sk, kd);
             add_outer(dv, dk, S, b, vd, kd);
+        } else if (variant == ORACLE_GDN2) {
+            /* S <- S diag(alpha) (I - (e * k) k^T) + (w * v) k^T, with the
+             * erase gate e [d_k] and then the write gate w [d_v] in beta */
+            const float *gate = beta + row * (size_t)(dk + dv);
+            for (int j = 0; j < dk; ++j) {
+                al[j] = exp((double)g[row * dk + j]);
+                ek[j] = (double)gate[j] * kd[j];
+            }
+            for (int i = 0; i < dv; ++i)
+                wv[i] = (double)gate[dk + i] * vd[i];
+            scale_columns(dv, dk, S, al);         /* S diag(alpha)      */
+            matvec(dv, dk, S, ek, Sk);            /* S diag(alpha) (e * k) */
+            add_outer(dv, dk, S, -1.0, Sk, kd);   /* - (S diag(alpha) (e * k)) k^T */
+            add_outer(dv, dk, S, 1.0, wv, kd);    /* + (w * v) k^T      */
         } else {
             /* S <- S diag(w) + v k^T */
             for (int j = 0; j < dk; ++j)
@@ -145,8 +168,9 @@ static void run_one(int variant, int64_t pair, int64_t n_pairs, int dk, int dv, 
  *   S0      [n_pairs, d_v, d_k] float32, or NULL for zero initial states
  *   q, k    [T, n_pairs, d_k]   float32 (exact bf16/fp32 input values)
  *   v       [T, n_pairs, d_v]   float32
- *   g       [T, n_pairs] (GDN) or [T, n_pairs, d_k] (KDA, RWKV6) float32 log-decay
- *   beta    [T, n_pairs] float32; ignored (may be NULL) for RWKV6
+ *   g       [T, n_pairs] (GDN) or [T, n_pairs, d_k] (KDA, RWKV6, gated) float32 log-decay
+ *   beta    [T, n_pairs] float32; [T, n_pairs, d_k + d_v] for the gated form
+ *           (erase gate, then write gate); ignored (may be NULL) for RWKV6
  *   t_start [n_pairs] int32 first step a state takes, or NULL (all start at 0);
  *           outputs before it are 0
  *   o       [T, n_pairs, d_v] float64 out
@@ -160,12 +184,12 @@ int oracle_run(int variant, int64_t n_pairs, int d_k, int d_v, int T, const floa
                const float *beta, const int32_t *t_start, double *o, double *S_out,
                int n_threads)
 {
-    if (variant < ORACLE_GDN || variant > ORACLE_RWKV6 || n_pairs < 0 || d_k <= 0 ||
+    if (variant < ORACLE_GDN || variant > ORACLE_GDN2 || n_pairs < 0 || d_k <= 0 ||
         d_v <= 0 || T < 0 || !q || !k || !v || !g || !o || !S_out)
         return -1;
     if (variant != ORACLE_RWKV6 && !beta)
         return -1;
-    const size_t work_len = (size_t)3 * d_k + (size_t)3 * d_v;
+    const size_t work_len = (size_t)4 * d_k + (size_t)4 * d_v;
     int failed = 0;
 #ifdef _OPENMP
     if (n_threads > 0)

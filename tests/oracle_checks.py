@@ -9,8 +9,10 @@ must fail at least one check.
 
 Recurrences (state ``S`` is ``d_v x d_k``, ``alpha = exp(g)``):
 GDN ``S' = alpha S (I - beta k k^T) + beta v k^T``; KDA the same with
-``S diag(alpha)``; RWKV6-style ``S' = S diag(w) + v k^T``; readout
-``o = S' q``.
+``S diag(alpha)``; RWKV6-style ``S' = S diag(w) + v k^T``; the gated form
+``S' = S diag(alpha) (I - (e * k) k^T) + (w * v) k^T`` (erase gate ``e`` on
+the key channels, write gate ``w`` on the value channels, passed as
+``beta = [e, w]``); readout ``o = S' q``.
 """
 from __future__ import annotations
 
@@ -22,8 +24,8 @@ import numpy as np
 import oracle
 from oracle import exact
 
-GDN, KDA, RWKV6 = 0, 1, 2
-VARIANTS = (GDN, KDA, RWKV6)
+GDN, KDA, RWKV6, GDN2 = 0, 1, 2, 3
+VARIANTS = (GDN, KDA, RWKV6, GDN2)
 
 
 def _dyadic(rng, shape, den=8, lo=-8, hi=8):
@@ -67,8 +69,20 @@ def _random_case(variant, rng, T, dk, dv):
     k = _dyadic(rng, (T, dk))
     v = _dyadic(rng, (T, dv))
     g = (-rng.integers(0, 9, size=(T,) if variant == GDN else (T, dk)) / 16).astype(np.float32)
-    beta = None if variant == RWKV6 else (rng.integers(1, 9, size=T) / 8).astype(np.float32)
+    if variant == GDN2:
+        beta = (rng.integers(0, 9, size=(T, dk + dv)) / 8).astype(np.float32)
+    else:
+        beta = None if variant == RWKV6 else (rng.integers(1, 9, size=T) / 8).astype(np.float32)
     return S0, q, k, v, g, beta
+
+
+def _betas_exact(variant, beta, dk):
+    """Write strengths as exact rationals (the gated form: (erase, write) pairs)."""
+    if beta is None:
+        return None
+    if variant == GDN2:
+        return [([Fr(float(x)) for x in b[:dk]], [Fr(float(x)) for x in b[dk:]]) for b in beta]
+    return [Fr(float(b)) for b in beta]
 
 
 def _fr_mat(a):
@@ -91,7 +105,7 @@ def check_bruteforce(lib_path=None):
         for (T, dk, dv) in ((6, 4, 3), (5, 3, 4)):
             S0, q, k, v, g, beta = _random_case(variant, rng, T, dk, dv)
             alphas = [_alpha_exact(variant, g[t]) for t in range(T)]
-            betas = None if beta is None else [Fr(float(b)) for b in beta]
+            betas = _betas_exact(variant, beta, dk)
             outs_x, S_x = exact.run_stepwise(variant, _fr_mat(S0), _fr_vecs(q), _fr_vecs(k),
                                              _fr_vecs(v), alphas, betas)
             S_brute = exact.run_product_expansion(variant, _fr_mat(S0), _fr_vecs(k),
@@ -131,6 +145,8 @@ def check_identity(lib_path=None):
         g = np.zeros((T,) if variant == GDN else (T, d), np.float32)
         if variant == RWKV6:
             v, beta = np.zeros((T, d), np.float32), None
+        elif variant == GDN2:
+            v, beta = rng.standard_normal((T, d)).astype(np.float32), np.zeros((T, 2 * d), np.float32)
         else:
             v, beta = rng.standard_normal((T, d)).astype(np.float32), np.zeros(T, np.float32)
         o, S = _run(variant, lib_path, q, k, v, g, beta, S0)
@@ -255,7 +271,51 @@ def check_late_start(lib_path=None):
             assert np.array_equal(o[sl, p], o1) and not o[: int(t0[p]), p].any()
 
 
+def check_gates_collapse_to_kda(lib_path=None):
+    """The gated form with erase and write gates equal to one scalar beta is KDA."""
+    rng = np.random.default_rng(11)
+    T, d = 10, 16
+    S0, q, k, v, g, beta = _random_case(KDA, rng, T, d, d)
+    gates = np.repeat(beta[:, None], 2 * d, axis=1)
+    o1, S1 = _run(KDA, lib_path, q, k, v, g, beta, S0)
+    o2, S2 = _run(GDN2, lib_path, q, k, v, g, gates, S0)
+    assert np.abs(S1 - S2).max() <= 1e-13 * max(1, np.abs(S1).max())
+    assert np.abs(o1 - o2).max() <= 1e-13 * max(1, np.abs(o1).max())
+
+
+def check_gated_no_erase(lib_path=None):
+    """Erase gate 0: S_T = S_0 diag(P_T) + sum_t (w_t * v_t)(k_t * P_T / P_t)^T, P_t = prod_{m<=t} alpha_m."""
+    rng = np.random.default_rng(12)
+    T, dk, dv = 9, 8, 6
+    S0 = rng.standard_normal((dv, dk)).astype(np.float32)
+    q = rng.standard_normal((T, dk)).astype(np.float32)
+    k = rng.standard_normal((T, dk)).astype(np.float32)
+    v = rng.standard_normal((T, dv)).astype(np.float32)
+    g = (-rng.random((T, dk))).astype(np.float32)
+    w = rng.random((T, dv)).astype(np.float32)
+    gates = np.concatenate([np.zeros((T, dk), np.float32), w], axis=1)
+    _, S = _run(GDN2, lib_path, q, k, v, g, gates, S0)
+    P = np.cumprod(np.exp(g.astype(np.float64)), axis=0)
+    ref = S0.astype(np.float64) * P[-1][None, :]
+    for t in range(T):
+        ref += np.outer(w[t].astype(np.float64) * v[t], k[t].astype(np.float64) * P[-1] / P[t])
+    assert np.abs(S - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def check_gated_write_invariant(lib_path=None):
+    """Both gates 1, unit key: S_t k_t = v_t for any per-key decay."""
+    rng = np.random.default_rng(13)
+    T, d = 20, 64
+    k = _unit_keys(rng, T, d)
+    v = rng.standard_normal((T, d)).astype(np.float32)
+    S0 = rng.standard_normal((d, d)).astype(np.float32)
+    g = (-rng.random((T, d))).astype(np.float32)
+    o, _ = _run(GDN2, lib_path, k, k, v, g, np.ones((T, 2 * d), np.float32), S0)
+    assert np.abs(o - v).max() <= 1e-12
+
+
 ALL_CHECKS = [check_bruteforce, check_write_invariant, check_identity,
               check_additive_closed_form, check_pure_decay, check_orthonormal_keys,
               check_channel_decay_collapses, check_reflection_norm,
-              check_readout_after_update, check_late_start]
+              check_readout_after_update, check_late_start, check_gates_collapse_to_kda,
+              check_gated_no_erase, check_gated_write_invariant]

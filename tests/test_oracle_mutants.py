@@ -42,6 +42,12 @@ MUTANTS = [
     ("outer-transposed-index", "S[(size_t)i * dk + j] += c * a[i] * b[j];",
      "S[(size_t)i * dk + j] += c * a[j % dv] * b[i % dk];", 0),
     ("late-start-ignored", "if (t < t_first) {", "if (t < 0) {", 0),
+    ("gated-no-erase-gate", "ek[j] = (double)gate[j] * kd[j];", "ek[j] = kd[j];", 0),
+    ("gated-no-write-gate", "wv[i] = (double)gate[dk + i] * vd[i];", "wv[i] = vd[i];", 0),
+    ("gated-write-gate-from-erase", "wv[i] = (double)gate[dk + i] * vd[i];",
+     "wv[i] = (double)gate[i % dk] * vd[i];", 0),
+    ("gated-erase-along-gated-key", "add_outer(dv, dk, S, -1.0, Sk, kd);",
+     "add_outer(dv, dk, S, -1.0, Sk, ek);", 0),
 ]
 
 

@@ -14,7 +14,7 @@ import pytest
 import oracle
 from oracle import exact
 
-from oracle_checks import ALL_CHECKS, GDN, KDA, RWKV6, VARIANTS
+from oracle_checks import ALL_CHECKS, GDN, GDN2, KDA, RWKV6, VARIANTS
 
 
 @pytest.mark.parametrize("check", ALL_CHECKS, ids=lambda f: f.__name__)
@@ -48,11 +48,18 @@ def _exact_case(variant, rng, T, d):
         alphas = [Fr(int(x), 8) for x in rng.integers(1, 9, size=T)]
     else:
         alphas = [[Fr(int(x), 8) for x in rng.integers(1, 9, size=d)] for _ in range(T)]
-    betas = None if variant == RWKV6 else [Fr(int(x), 8) for x in rng.integers(0, 9, size=T)]
+    if variant == GDN2:
+        betas = [([Fr(int(x), 8) for x in rng.integers(0, 9, size=d)],
+                  [Fr(int(x), 8) for x in rng.integers(0, 9, size=d)]) for _ in range(T)]
+    else:
+        betas = None if variant == RWKV6 else [Fr(int(x), 8) for x in rng.integers(0, 9, size=T)]
     return S0, qs, ks, vs, alphas, betas
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+WY_VARIANTS = (GDN, KDA, RWKV6)     # the compact-WY log is built for these
+
+
+@pytest.mark.parametrize("variant", WY_VARIANTS)
 @pytest.mark.parametrize("L", [1, 2, 3, 5])
 def test_deferred_equals_eager_exactly(variant, L):
     """Base + log with q-chain readout and WY merge == the eager recurrence, exactly."""
@@ -66,7 +73,7 @@ def test_deferred_equals_eager_exactly(variant, L):
     assert fill == T % L
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", WY_VARIANTS)
 def test_wy_merge_matches_replay(variant):
     """One WY merge of n entries equals n eager steps from the base, exactly."""
     rng = np.random.default_rng(200 + variant)
@@ -112,21 +119,25 @@ def test_exact_model_matches_oracle_on_floats():
         S0 = (rng.integers(-4, 5, size=(d, d)) / 4).astype(np.float32)
         q, k, v = ((rng.integers(-8, 9, size=(T, d)) / 8).astype(np.float32) for _ in range(3))
         g = (-rng.integers(0, 5, size=(T,) if variant == GDN else (T, d)) / 8).astype(np.float32)
-        beta = None if variant == RWKV6 else (rng.integers(0, 9, size=T) / 8).astype(np.float32)
+        if variant == GDN2:
+            beta = (rng.integers(0, 9, size=(T, 2 * d)) / 8).astype(np.float32)
+            b_exact = [([Fr(float(x)) for x in b[:d]], [Fr(float(x)) for x in b[d:]]) for b in beta]
+        else:
+            beta = None if variant == RWKV6 else (rng.integers(0, 9, size=T) / 8).astype(np.float32)
+            b_exact = None if beta is None else [Fr(float(b)) for b in beta]
         if variant == GDN:
             alphas = [Fr(math.exp(float(x))) for x in g]
         else:
             alphas = [[Fr(math.exp(float(x))) for x in row] for row in g]
         fr = lambda a: [[Fr(float(x)) for x in row] for row in a]
-        o_x, S_x = exact.run_stepwise(variant, fr(S0), fr(q), fr(k), fr(v), alphas,
-                                      None if beta is None else [Fr(float(b)) for b in beta])
+        o_x, S_x = exact.run_stepwise(variant, fr(S0), fr(q), fr(k), fr(v), alphas, b_exact)
         o, S = oracle.run(variant, q[:, None], k[:, None], v[:, None],
                           g[:, None], None if beta is None else beta[:, None], S0[None])
         Sx = np.array([[float(x) for x in r] for r in S_x])
         assert np.abs(S[0] - Sx).max() <= 1e-12 * max(1, np.abs(Sx).max())
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", WY_VARIANTS)
 @pytest.mark.parametrize("n", [1, 2, 3, 6])
 def test_wy_readout_equals_chain_readout(variant, n):
     """The compact-WY readout (R = (I + N)^{-1}, no sequential chain) equals the
@@ -176,7 +187,7 @@ def test_af_deferred_equals_eager_exactly(variant, L):
     assert fill == T % L
 
 
-@pytest.mark.parametrize("variant", VARIANTS)
+@pytest.mark.parametrize("variant", WY_VARIANTS)
 def test_af_factors_are_wy_solve_columns(variant):
     """The factors appended step by step equal the columns of the WY merge's
     triangular solve over the same entries: two derivations, one result."""
@@ -197,7 +208,10 @@ def test_additive_factor_against_recurrence_and_exact_model():
         S0 = rng.standard_normal((P, d, d)).astype(np.float32)
         q, k, v = (rng.standard_normal((1, P, d)).astype(np.float32) for _ in range(3))
         g = (-rng.random((1, P) if variant == GDN else (1, P, d))).astype(np.float32)
-        beta = None if variant == RWKV6 else rng.random((1, P)).astype(np.float32)
+        if variant == GDN2:
+            beta = rng.random((1, P, 2 * d)).astype(np.float32)
+        else:
+            beta = None if variant == RWKV6 else rng.random((1, P)).astype(np.float32)
         _, S1 = oracle.run(variant, q, k, v, g, beta, S0)
         a = oracle.additive_factor(variant, S0, k[0], v[0], g[0], None if beta is None else beta[0])
         alpha = np.exp(g[0].astype(np.float64))
@@ -208,12 +222,29 @@ def test_additive_factor_against_recurrence_and_exact_model():
         S0x = (rng.integers(-4, 5, size=(d, d)) / 4).astype(np.float32)
         kx, vx = ((rng.integers(-8, 9, size=d) / 8).astype(np.float32) for _ in range(2))
         gx = (-rng.integers(0, 5, size=() if variant == GDN else (d,)) / 8).astype(np.float32)
-        bx = np.float32(rng.integers(0, 9) / 8)
+        if variant == GDN2:
+            bx = (rng.integers(0, 9, size=2 * d) / 8).astype(np.float32)
+            b_exact = ([Fr(float(x)) for x in bx[:d]], [Fr(float(x)) for x in bx[d:]])
+        else:
+            bx = np.float32(rng.integers(0, 9) / 8)
+            b_exact = Fr(float(bx))
         alpha_x = Fr(math.exp(float(gx))) if variant == GDN else [Fr(math.exp(float(x))) for x in gx]
         ax, _, _ = exact.af_append(variant, [[Fr(float(x)) for x in r] for r in S0x], [],
                                    [Fr(float(x)) for x in kx], [Fr(float(x)) for x in vx],
-                                   alpha_x, Fr(float(bx)))
+                                   alpha_x, b_exact)
         af = oracle.additive_factor(variant, S0x[None], kx[None], vx[None],
                                     np.asarray(gx)[None], np.asarray([bx]))
         ref = np.array([float(x) for x in ax])
         assert np.abs(af[0] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_gated_af_equals_kda_when_gates_collapse():
+    """Additive-factor deferred run of the gated form with both gates equal to
+    KDA's scalar beta reproduces KDA's eager run exactly."""
+    rng = np.random.default_rng(700)
+    T, d = 7, 3
+    S0, qs, ks, vs, alphas, betas = _exact_case(KDA, rng, T, d)
+    gates = [([b] * d, [b] * d) for b in betas]
+    o_k, S_k = exact.run_stepwise(KDA, S0, qs, ks, vs, alphas, betas)
+    o_g, S_g, _, _ = exact.af_deferred_run(GDN2, S0, qs, ks, vs, alphas, gates, 3)
+    assert o_g == o_k and S_g == S_k

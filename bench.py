@@ -49,7 +49,7 @@ def byte_model(wl: W.Workload):
     dk, dv = wl.d_k, wl.d_v
     St = 4 * dv * dk                                   # fp32 state
     g = 4 * dk if wl.channel_decay else 4
-    b = 4 if wl.has_beta else 0
+    b = 4 * wl.beta_width if wl.has_beta else 0       # beta (gated: erase + write gates)
     In = (2 * dk + dv) * es + g + b                    # q, k, v, g, beta
     Out = 4 * dv                                       # fp32 o
     E = (dk + dv) * es + g + b                         # one log entry
@@ -207,6 +207,9 @@ def main(argv=None):
     if not wl.has_beta:
         # the additive variant's log already stores additive factors: af == log
         paths = [p for p in paths if not p.startswith("af")]
+    if wl.variant == W.GDN2:
+        # the gated form's log is built in the factor form only
+        paths = [p for p in paths if p not in ("log", "log-replay", "log-fused")]
     m0 = byte_model(wl)
     log(f"[bench] {wl.name}: variant {W.VARIANT_NAMES[wl.variant]}, {P} states, d={d}, L={L}, "
         f"steps {prefix}+{Wu}+{K}, inputs {wl.dtype}")
@@ -219,7 +222,8 @@ def main(argv=None):
     Kt = torch.empty_like(Q)
     V = torch.empty_like(Q)
     G = torch.empty((T, U, H, d) if wl.channel_decay else (T, U, H), dtype=torch.float32, device=dev)
-    Bb = torch.empty((T, U, H), dtype=torch.float32, device=dev) if wl.has_beta else None
+    bshape = (T, U, H) if wl.beta_width == 1 else (T, U, H, wl.beta_width)
+    Bb = torch.empty(bshape, dtype=torch.float32, device=dev) if wl.has_beta else None
     # oracle sample: calibrate its speed, then pick how many states it takes
     sample_cap = P
     if not args.no_cpu_baseline:
@@ -254,7 +258,7 @@ def main(argv=None):
                 sv.append(s.v_f32.reshape(P, d)[sample])
                 sg.append(s.g.reshape(P, -1)[sample] if wl.channel_decay else s.g.reshape(P)[sample])
                 if s.beta is not None:
-                    sb.append(s.beta.reshape(P)[sample])
+                    sb.append(s.beta.reshape((P,) if wl.beta_width == 1 else (P, -1))[sample])
     S0 = W.initial_state(wl, args.seed)
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s "

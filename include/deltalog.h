@@ -22,6 +22,11 @@
  *   GDN    S' = alpha S (I - beta k k^T) + beta v k^T
  *   KDA    S' = S diag(alpha) (I - beta k k^T) + beta v k^T
  *   RWKV6  S' = S diag(w) + v k^T          (w = exp(g), per key channel)
+ *   GDN2   S' = S diag(alpha) (I - (e * k) k^T) + (w * v) k^T
+ *          (the gated form of the Gated DeltaNet-2 and FG2-GDN abstracts:
+ *          KDA's beta split into a channel-wise erase gate e on the key
+ *          channels and a write gate w on the value channels; KDA when both
+ *          are the same scalar)
  *   every step reads out o = S' q.
  *
  * Memory.  The caller owns all device memory (e.g. torch tensors): one state
@@ -59,13 +64,21 @@ extern "C" {
 typedef enum {
     DL_OK = 0,
     DL_ERR_INVALID = 1,      /* null or misaligned pointer, bad count, argument wrong for the variant */
-    DL_ERR_UNSUPPORTED = 2,  /* well-formed but not built: d_k != d_v, d not in {64, 128}, L > 64 */
+    DL_ERR_UNSUPPORTED = 2,  /* well-formed but not built: d_k != d_v, d not in {64, 128}, L > 64,
+                              * a GDN2 log in the WY form */
     DL_ERR_SIZE = 3,         /* caller memory smaller than dl_state_bytes() */
     DL_ERR_LAUNCH = 4,       /* the HIP runtime rejected a launch or copy */
     DL_ERR_STATE = 5         /* dl_state_check found device flags set */
 } dl_status;
 
-typedef enum { DL_GDN = 0, DL_KDA = 1, DL_RWKV6 = 2 } dl_variant;
+typedef enum {
+    DL_GDN = 0,              /* head-wise decay, delta rule */
+    DL_KDA = 1,              /* per-key decay, delta rule */
+    DL_RWKV6 = 2,            /* per-key decay, raw-value updates */
+    DL_GDN2 = 3              /* per-key decay, delta rule with a channel-wise erase
+                              * gate e (key channels) and write gate w (value
+                              * channels); DeltaLog only with DL_LOG_FACTORS */
+} dl_variant;
 typedef enum { DL_F32 = 0, DL_BF16 = 1 } dl_dtype;
 
 /* What the log stores per pending step (dl_desc.log_form). */
@@ -109,7 +122,7 @@ typedef struct {
  *   log_k    [units, H, L, d_k] in_dtype -- logged keys, bit copies of the inputs
  *   log_v    [units, H, L, d_v] in_dtype -- logged values; under DL_LOG_FACTORS
  *            (GDN, KDA) fp32 -- the factors a_t
- *   log_g    [units, H, L] (GDN) or [units, H, L, d_k] (KDA, RWKV6) fp32 -- the
+ *   log_g    [units, H, L] (GDN) or [units, H, L, d_k] (KDA, RWKV6, GDN2) fp32 -- the
  *            log-decay accumulated from the log's first entry through each
  *            entry (Lam_j = Lam_{j-1} + g_j in fp32, Lam_{-1} = 0)
  *   log_beta [units, H, L] fp32 (NULL for RWKV6 and under DL_LOG_FACTORS)
@@ -159,10 +172,12 @@ dl_status dl_state_view(const dl_state *st, dl_state_ptrs *out);
  * write the whole state back and emit o = S' q.  The unit's log must be
  * empty (else DL_FLAG_LOG_NONEMPTY).
  *   q, k   [rows, H, d_k] in_dtype         v [rows, H, d_v] in_dtype
- *   g      [rows, H] (GDN) or [rows, H, d_k] (KDA, RWKV6) fp32 log-decay
- *   beta   [rows, H] fp32 (GDN, KDA; ignored and may be NULL for RWKV6)
+ *   g      [rows, H] (GDN) or [rows, H, d_k] (KDA, RWKV6, GDN2) fp32 log-decay
+ *   beta   [rows, H] fp32 (GDN, KDA; ignored and may be NULL for RWKV6);
+ *          GDN2: [rows, H, d_k + d_v] fp32, the erase gate then the write gate
  *   o      [rows, H, d_v] fp32 output (must not alias any input or the state)
- * q, k, v, g, o must be 16-byte aligned; beta and slot_idx 4-byte aligned. */
+ * q, k, v, g, o must be 16-byte aligned; beta and slot_idx 4-byte aligned
+ * (beta 16-byte aligned for GDN2). */
 dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_idx,
                                const void *q, const void *k, const void *v, const float *g,
                                const float *beta, float *o, void *stream);

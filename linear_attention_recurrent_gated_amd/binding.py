@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libdeltalog.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "deltalog.h")
 
 DL_OK, DL_ERR_INVALID, DL_ERR_UNSUPPORTED, DL_ERR_SIZE, DL_ERR_LAUNCH, DL_ERR_STATE = range(6)
-DL_GDN, DL_KDA, DL_RWKV6 = 0, 1, 2
+DL_GDN, DL_KDA, DL_RWKV6, DL_GDN2 = 0, 1, 2, 3
 DL_F32, DL_BF16 = 0, 1
 DL_MERGE_FULL, DL_MERGE_ALL = 0, 1
 DL_LOG_WY, DL_LOG_FACTORS = 0, 1
@@ -254,7 +254,8 @@ class DecodeState:
         gshape = (rows, H) if self.variant == DL_GDN else (rows, H, d)
         assert g.dtype == t.float32 and g.is_contiguous() and tuple(g.shape) == gshape
         if self.variant != DL_RWKV6:
-            assert beta.dtype == t.float32 and beta.is_contiguous() and beta.shape == (rows, H)
+            bshape = (rows, H, 2 * d) if self.variant == DL_GDN2 else (rows, H)
+            assert beta.dtype == t.float32 and beta.is_contiguous() and tuple(beta.shape) == bshape
 
     def _out(self, rows, o):
         if o is None:

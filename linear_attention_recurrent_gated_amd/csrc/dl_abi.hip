@@ -46,7 +46,7 @@ struct Layout {
 dl_status check_desc(const dl_desc *d) {
     if (!d)
         return fail(DL_ERR_INVALID, "descriptor is NULL");
-    if (d->variant < DL_GDN || d->variant > DL_RWKV6)
+    if (d->variant < DL_GDN || d->variant > DL_GDN2)
         return fail(DL_ERR_INVALID, "unknown variant %d", d->variant);
     if (d->units < 1 || d->heads < 1)
         return fail(DL_ERR_INVALID, "units (%d) and heads (%d) must be >= 1", d->units, d->heads);
@@ -64,6 +64,8 @@ dl_status check_desc(const dl_desc *d) {
         return fail(DL_ERR_UNSUPPORTED, "d = %d is not built (64 or 128)", d->d_k);
     if (d->log_len > 64)
         return fail(DL_ERR_UNSUPPORTED, "log_len %d > 64 is not built", d->log_len);
+    if (d->variant == DL_GDN2 && d->log_len > 0 && d->log_form != DL_LOG_FACTORS)
+        return fail(DL_ERR_UNSUPPORTED, "the gated variant's log is built in the factor form only");
     const size_t pairs = (size_t)d->units * (size_t)d->heads;
     if (pairs > (size_t)0x7fffffff)
         return fail(DL_ERR_INVALID, "units * heads too large");
@@ -134,8 +136,9 @@ dl_status check_step_args(const dl_state *st, int32_t rows, const int32_t *slot_
     if (st->desc.variant != DL_RWKV6) {
         if (!beta)
             return fail(DL_ERR_INVALID, "beta is required for the delta-rule variants");
-        if (!aligned(beta, 4))
-            return fail(DL_ERR_INVALID, "beta must be 4-byte aligned");
+        const int ba = st->desc.variant == DL_GDN2 ? 16 : 4;
+        if (!aligned(beta, ba))
+            return fail(DL_ERR_INVALID, "beta must be %d-byte aligned", ba);
     }
     return DL_OK;
 }
@@ -389,7 +392,8 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
     const double St = 4.0 * dv * dk;
     const bool af = factors_form(d);
     const double gb = d.variant == DL_GDN ? 4.0 : 4.0 * dk;       // decay bytes per entry
-    const double bb = d.variant == DL_RWKV6 ? 0.0 : 4.0;          // beta bytes per input
+    const double bb = d.variant == DL_RWKV6 ? 0.0                 // beta bytes per input
+                      : d.variant == DL_GDN2 ? 4.0 * (dk + dv) : 4.0;
     const double In = (2.0 * dk + dv) * es + gb + bb;
     const double Out = 4.0 * dv;
     // logged entry: key, value (fp32 factor under the additive-factor form), decay, beta

@@ -19,7 +19,7 @@
 
 namespace dl {
 
-enum Variant { GDN = DL_GDN, KDA = DL_KDA, RWKV6 = DL_RWKV6 };
+enum Variant { GDN = DL_GDN, KDA = DL_KDA, RWKV6 = DL_RWKV6, GDN2 = DL_GDN2 };
 
 // Device-side view of one state block (all pointers into caller memory).
 struct Params {
@@ -219,6 +219,8 @@ struct AfPlan {
     int off_lc;    // per-key decays: Lam of the newest entry, D floats
     int off_qe, off_ke;               // E q and E k, D floats each
     int off_v;     // the step's value row, D elements (up to 4 bytes each)
+    int off_w;     // gated form: the write gate row, D floats
+    int off_ek;    // gated form: the erase-gated key e * k, D floats
     int bytes;
 };
 
@@ -236,7 +238,9 @@ __host__ __device__ inline AfPlan af_plan(int D, int L, bool merges) {
     p.off_qe = p.off_lc + D * 4;
     p.off_ke = p.off_qe + D * 4;
     p.off_v = p.off_ke + D * 4;
-    p.bytes = p.off_v + D * 4;
+    p.off_w = p.off_v + D * 4;
+    p.off_ek = p.off_w + D * 4;
+    p.bytes = p.off_ek + D * 4;
     return p;
 }
 

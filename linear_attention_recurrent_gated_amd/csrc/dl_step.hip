@@ -4,10 +4,13 @@
 // Operators (the DeltaLog page, "DeltaLog: Deferred Materialization of
 // Recurrent States for Linear Attention Decoding", Technical Summary, Kernel
 // Implementation): GDN (head-wise scalar decay + delta-rule correction), KDA
-// (per-key decay + correction), RWKV6 (per-key decay, raw-value update).
+// (per-key decay + correction), RWKV6 (per-key decay, raw-value update); and
+// the gated form of the Gated DeltaNet-2 abstract (CARVE page, Explore
+// similar work), KDA with a channel-wise erase gate e and write gate w.
 // Written with S (d_v x d_k), alpha = exp(g):
 //   delta rule: u = S (alpha.k), p = S (alpha.q), delta = beta (v - u),
 //               S' = S diag(alpha) + delta k^T,  o = p + delta (k.q)
+//   gated:      u = S (alpha.e.k), delta = w.v - u, the rest as above
 //   additive:   S' = S diag(w) + v k^T,          o = S (w.q) + v (k.q)
 // Both are the update formulas multiplied out so that the state is read and
 // written exactly once per step.
@@ -76,20 +79,25 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
         for (int m = 0; m < SH::NCH; ++m)
             st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
-    float kc[SH::FPL], qc[SH::FPL], ac[SH::FPL];
+    float kc[SH::FPL], qc[SH::FPL], ac[SH::FPL], ec[SH::FPL];
+    const float *gate = beta + (size_t)pr * 2 * D;   // gated: erase gate, then write gate
 #pragma unroll
     for (int m = 0; m < SH::NCH; ++m) {
         f4_to(kc + 4 * m, Elem<T>::load4(k + io + col_of(s, m, 0)));
         f4_to(qc + 4 * m, Elem<T>::load4(q + io + col_of(s, m, 0)));
         if constexpr (V != GDN)
             f4_to(ac + 4 * m, *reinterpret_cast<const float4 *>(g + io + col_of(s, m, 0)));
+        if constexpr (V == GDN2)
+            f4_to(ec + 4 * m, *reinterpret_cast<const float4 *>(gate + col_of(s, m, 0)));
     }
     const float g_s = (V == GDN) ? g[pr] : 0.f;
-    const float b = (V == RWKV6) ? 1.f : beta[pr];
-    float vr[SH::ITER];
+    const float b = (V == RWKV6 || V == GDN2) ? 1.f : beta[pr];
+    float vr[SH::ITER], wr[SH::ITER];
 #pragma unroll
-    for (int it = 0; it < SH::ITER; ++it)
+    for (int it = 0; it < SH::ITER; ++it) {
         vr[it] = Elem<T>::load1(v + io + wave * SH::RPW + it * 8 + grp);
+        wr[it] = (V == GDN2) ? gate[D + wave * SH::RPW + it * 8 + grp] : 1.f;
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (fill != 0) {
         reject_row(P, orow, D, DL_FLAG_LOG_NONEMPTY);
@@ -110,7 +118,7 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
 #pragma unroll
     for (int f = 0; f < SH::FPL; ++f) {
         kq += kc[f] * qc[f];
-        ak[f] = (V == GDN) ? kc[f] : ac[f] * kc[f];
+        ak[f] = (V == GDN) ? kc[f] : (V == GDN2) ? ac[f] * ec[f] * kc[f] : ac[f] * kc[f];
         aq[f] = (V == GDN) ? qc[f] : ac[f] * qc[f];
     }
     kq = sum8(kq);
@@ -134,7 +142,7 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
             u *= alpha;
             p *= alpha;
         }
-        const float d = (V == RWKV6) ? vr[it] : b * (vr[it] - u);
+        const float d = (V == RWKV6) ? vr[it] : (V == GDN2) ? wr[it] * vr[it] - u : b * (vr[it] - u);
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m) {
             float sv[4] = {st[it][m].x, st[it][m].y, st[it][m].z, st[it][m].w};
@@ -778,6 +786,21 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
         return FN<RWKV6, 64, float>(__VA_ARGS__);                                        \
     } while (0)
 
+// the eager step also runs the gated form
+#define DL_DISPATCH_EAGER(P, FN, ...)                                                    \
+    do {                                                                                 \
+        if ((P).variant == DL_GDN2) {                                                    \
+            const bool bf = (P).dtype == DL_BF16;                                        \
+            if ((P).D == 128) {                                                          \
+                if (bf) return FN<GDN2, 128, uint16_t>(__VA_ARGS__);                     \
+                return FN<GDN2, 128, float>(__VA_ARGS__);                                \
+            }                                                                            \
+            if (bf) return FN<GDN2, 64, uint16_t>(__VA_ARGS__);                          \
+            return FN<GDN2, 64, float>(__VA_ARGS__);                                     \
+        }                                                                                \
+        DL_DISPATCH(P, FN, __VA_ARGS__);                                                 \
+    } while (0)
+
 template <int V, int D, typename T>
 static hipError_t eager_t(const Params &P, int rows, const int *slot_idx, const void *q,
                           const void *k, const void *v, const float *g, const float *beta,
@@ -846,7 +869,7 @@ static hipError_t readout_t(const Params &P, int rows, const int *slot_idx, cons
 hipError_t launch_eager(const Params &P, int rows, const int *slot_idx, const void *q,
                         const void *k, const void *v, const float *g, const float *beta,
                         float *o, const Launch &ln) {
-    DL_DISPATCH(P, eager_t, P, rows, slot_idx, q, k, v, g, beta, o, ln);
+    DL_DISPATCH_EAGER(P, eager_t, P, rows, slot_idx, q, k, v, g, beta, o, ln);
 }
 
 hipError_t launch_log_step(const Params &P, int rows, const int *slot_idx, const void *q,

@@ -19,6 +19,13 @@
 // (k_j D(j, c))^T.  The factors are fp32 (they are results, not copies of
 // inputs); the keys stay bit copies.
 //
+// The gated form (Gated DeltaNet-2 abstract, CARVE page, Explore similar
+// work: a channel-wise erase gate e on the key channels and write gate w on
+// the value channels) keeps the update rank one along k:
+//   a_t = w_t * v_t - S_{t-1} (alpha_t e_t k_t),
+// so only the read direction (e k for k in x and u_j) and the value term
+// change; the log, readout and merge are the same as KDA's.
+//
 // Same workgroup shape as the compact-WY step (dl_step.hip): one workgroup of
 // four waves per (row, head), S0 rows in registers (lane groups of 8, lane s
 // holding the columns 4s + 32m + e).  Each logged key and decay is used by
@@ -151,14 +158,17 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
 // otherwise a readout of base + log.  FUSE: the step that fills the log
 // also merges it (fill back to 0).  With bf16 inputs and logs of up to 32
 // entries the kernel is held to the registers of four waves per SIMD (four
-// workgroups per CU), except where that spills on the hot path (per-key
-// decays, 32 entries, merge in the step), which runs three.
+// workgroups per CU), except where that spills on the hot path (32 entries
+// with per-key decays and the merge in the step, or with gates), which runs
+// three.
 template <int V, int D, typename T, bool APPEND, int MV, bool NT, bool FUSE>
-__global__ void __launch_bounds__(256, (MV <= 4 && sizeof(T) == 2) ? ((V == KDA && FUSE && MV == 4) ? 3 : 4) : 1)
+__global__ void __launch_bounds__(256, (MV <= 4 && sizeof(T) == 2)
+                                          ? ((MV == 4 && (V == GDN2 || (V == KDA && FUSE))) ? 3 : 4)
+                                          : 1)
 af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
                const float *__restrict__ beta, float *__restrict__ o) {
-    static_assert(V == GDN || V == KDA, "delta-rule variants only");
+    static_assert(V == GDN || V == KDA || V == GDN2, "delta-rule variants only");
     using SH = Shape<D>;
     using KL = KeyLayout<D>;
     constexpr int G = KL::G, RP = KL::RP, PASS = 4 * RP;   // entries per pass of the four waves
@@ -214,11 +224,16 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     // ---- loads that need n: beta, this lane's logged keys (and decays) of
     //      the first pass(es), the staging of the factors and of the new
     //      value row, and (wave 0) Lam and the decayed q and k
-    const float b_in = APPEND ? beta[pr] : 0.f;
+    const float b_in = (APPEND && V != GDN2) ? beta[pr] : 0.f;
+    const float *gate = beta + (size_t)pr * 2 * D;   // gated: erase gate, then write gate
     if constexpr (APPEND) {
         constexpr int CPV = D * (int)sizeof(T) / 16;
         if (wave == 0 && lane < CPV)
             load_to_lds<16>(reinterpret_cast<const uint4 *>(v + io) + lane, smem + ap.off_v);
+        if constexpr (V == GDN2) {
+            if (wave == 1 && lane < D / 4)
+                load_to_lds<16>(reinterpret_cast<const uint4 *>(gate + D) + lane, smem + ap.off_w);
+        }
     }
     const int ct = APPEND ? n + 1 : n;   // entries the readout sees
     const int npass = (ct + PASS - 1) / PASS;
@@ -290,6 +305,15 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
             store8<float>(sqe + ch0, t);
             if constexpr (APPEND) {
                 unpack8<T>(kr.a, kr.b, t);
+                if constexpr (V == GDN2) {
+                    // the read direction of the gated form: e * k
+                    float e[8];
+                    load8<float>(gate + ch0, e);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        t[i] *= e[i];
+                    store8<float>(reinterpret_cast<float *>(smem + ap.off_ek) + ch0, t);
+                }
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     t[i] *= en[i];
@@ -301,6 +325,9 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     __syncthreads();    // 1: staged factors, Lam_c, per-entry factors, E q, E k
 
     const bool merging = FUSE && APPEND && n == L - 1;
+    float ekv[8];                        // gated: this lane's channels of e * k
+    if constexpr (APPEND && V == GDN2)
+        load8<float>(reinterpret_cast<const float *>(smem + ap.off_ek) + ch0, ekv);
     if (n > 0) {
 #pragma unroll
         for (int p = EARLY; p < NP; ++p)
@@ -336,7 +363,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
         for (int i = 0; i < 8; ++i) {
             ar += kd[i] * qv[i];
             if constexpr (APPEND)
-                au += kd[i] * kn[i];
+                au += kd[i] * ((V == GDN2) ? ekv[i] : kn[i]);
         }
         ar = group_sum<G>(ar);
         if constexpr (APPEND)
@@ -404,7 +431,9 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
         if constexpr (APPEND) {
             ax = sum8(ax);
             const float vr = Elem<T>::load1(reinterpret_cast<const T *>(smem + ap.off_v) + row);
-            const float an = b_in * (vr - ax);
+            const float an = (V == GDN2)
+                                 ? reinterpret_cast<const float *>(smem + ap.off_w)[row] * vr - ax
+                                 : b_in * (vr - ax);
             ao += rn * an;
             if (s == 1)
                 alog[row] = an;
@@ -451,7 +480,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
 template <int V, int D, typename T, bool NT>
 __global__ void __launch_bounds__(256) af_merge_kernel(Params P, const int *__restrict__ slot_idx,
                                                        int mode) {
-    static_assert(V == GDN || V == KDA, "delta-rule variants only");
+    static_assert(V == GDN || V == KDA || V == GDN2, "delta-rule variants only");
     using SH = Shape<D>;
     extern __shared__ __align__(16) unsigned char smem[];
     size_t pair;
@@ -527,21 +556,25 @@ __global__ void __launch_bounds__(256) af_merge_kernel(Params P, const int *__re
 #define DL_DISPATCH_AF(P, FN, ...)                                                       \
     do {                                                                                 \
         const bool bf = (P).dtype == DL_BF16;                                            \
-        const bool gdn = (P).variant == DL_GDN;                                          \
+        const int var = (P).variant;                                                     \
         if ((P).D == 128) {                                                              \
             if (bf) {                                                                    \
-                if (gdn) return FN<GDN, 128, uint16_t>(__VA_ARGS__);                     \
-                return FN<KDA, 128, uint16_t>(__VA_ARGS__);                              \
+                if (var == DL_GDN) return FN<GDN, 128, uint16_t>(__VA_ARGS__);           \
+                if (var == DL_KDA) return FN<KDA, 128, uint16_t>(__VA_ARGS__);           \
+                return FN<GDN2, 128, uint16_t>(__VA_ARGS__);                             \
             }                                                                            \
-            if (gdn) return FN<GDN, 128, float>(__VA_ARGS__);                            \
-            return FN<KDA, 128, float>(__VA_ARGS__);                                     \
+            if (var == DL_GDN) return FN<GDN, 128, float>(__VA_ARGS__);                  \
+            if (var == DL_KDA) return FN<KDA, 128, float>(__VA_ARGS__);                  \
+            return FN<GDN2, 128, float>(__VA_ARGS__);                                    \
         }                                                                                \
         if (bf) {                                                                        \
-            if (gdn) return FN<GDN, 64, uint16_t>(__VA_ARGS__);                          \
-            return FN<KDA, 64, uint16_t>(__VA_ARGS__);                                   \
+            if (var == DL_GDN) return FN<GDN, 64, uint16_t>(__VA_ARGS__);                \
+            if (var == DL_KDA) return FN<KDA, 64, uint16_t>(__VA_ARGS__);                \
+            return FN<GDN2, 64, uint16_t>(__VA_ARGS__);                                  \
         }                                                                                \
-        if (gdn) return FN<GDN, 64, float>(__VA_ARGS__);                                 \
-        return FN<KDA, 64, float>(__VA_ARGS__);                                          \
+        if (var == DL_GDN) return FN<GDN, 64, float>(__VA_ARGS__);                       \
+        if (var == DL_KDA) return FN<KDA, 64, float>(__VA_ARGS__);                       \
+        return FN<GDN2, 64, float>(__VA_ARGS__);                                         \
     } while (0)
 
 template <int V, int D, typename T, bool APPEND, int MV>

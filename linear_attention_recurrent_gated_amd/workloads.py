@@ -18,8 +18,9 @@ Recipe (all draws float64 from numpy's PCG64):
   ``SeedSequence([seed, cfg_id, tau])``; the initial state uses
   ``[seed, cfg_id, 2**32 - 1]`` and ragged log offsets ``[seed, cfg_id, 2**32 - 2]``;
 * draw order per step: q, k, v (each ``[units, H, d]``), the write-strength
-  logit (``[units, H]``, not drawn for the additive variant), the decay logit
-  (``[units, H]`` for head-wise decay, ``[units, H, d_k]`` for channel-wise);
+  logit (``[units, H]``, not drawn for the additive variant; ``[units, H,
+  d_k + d_v]`` -- erase gate, then write gate -- for the gated form), the decay
+  logit (``[units, H]`` for head-wise decay, ``[units, H, d_k]`` for channel-wise);
 * q and k are L2-normalised in float64 where the workload says so, then
   rounded to float32 (round-to-nearest-even) and, for bf16 storage, from
   float32 to bf16 (round-to-nearest-even);
@@ -36,8 +37,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-GDN, KDA, RWKV6 = 0, 1, 2
-VARIANT_NAMES = {GDN: "gdn", KDA: "kda", RWKV6: "rwkv6"}
+GDN, KDA, RWKV6, GDN2 = 0, 1, 2, 3
+VARIANT_NAMES = {GDN: "gdn", KDA: "kda", RWKV6: "rwkv6", GDN2: "gated"}
 
 _STATE_STREAM = 2**32 - 1
 _OFFSET_STREAM = 2**32 - 2
@@ -71,7 +72,12 @@ class Workload:
 
     @property
     def channel_decay(self) -> bool:
-        return self.variant in (KDA, RWKV6)
+        return self.variant in (KDA, RWKV6, GDN2)
+
+    @property
+    def beta_width(self) -> int:
+        """Write-strength values per (unit, head): 1, or erase + write gates."""
+        return self.d_k + self.d_v if self.variant == GDN2 else 1
 
     @property
     def has_beta(self) -> bool:
@@ -117,7 +123,13 @@ RWKV6_ADD = Workload("rwkv6-b512-h64-d64", 5, RWKV6, batch=512, layers=1, heads=
                      d_v=64, steps=1024, log_lens=(32,), dtype="bf16", qk_l2norm=False,
                      state_std=0.0, decay_mean=-0.5, decay_std=0.5)
 
-WORKLOADS = {w.cfg_id: w for w in (TINY_GDN, GDN_HYBRID, KDA_SWEEP, GDN_LARGE, RWKV6_ADD)}
+# Beyond the five: the gated form (channel-wise erase and write gates) at the
+# KDA sweep's shape and decay distribution.
+GATED = Workload("gated-b128-h32-d128", 6, GDN2, batch=128, layers=1, heads=32, d_k=128,
+                 d_v=128, steps=512, log_lens=(16,), dtype="bf16", qk_l2norm=True,
+                 state_std=0.0, decay_mean=-1.0, decay_std=1.0)
+
+WORKLOADS = {w.cfg_id: w for w in (TINY_GDN, GDN_HYBRID, KDA_SWEEP, GDN_LARGE, RWKV6_ADD, GATED)}
 
 
 # ----------------------------------------------------------------------------
@@ -178,7 +190,8 @@ class StepInputs:
 
     ``q/k/v``: stored arrays ``[units_total, H, d]`` (float32 or bf16 bits);
     ``*_f32``: the same values as float32; ``g``: float32 ``[units_total, H]``
-    or ``[units_total, H, d_k]``; ``beta``: float32 ``[units_total, H]`` or None.
+    or ``[units_total, H, d_k]``; ``beta``: float32 ``[units_total, H]``
+    (gated form: ``[units_total, H, d_k + d_v]``) or None.
     """
 
     q: np.ndarray
@@ -203,7 +216,9 @@ def draw_step(wl: Workload, tau: int, seed: int = 0) -> StepInputs:
     k = rng.standard_normal((U, H, wl.d_k))
     v = rng.standard_normal((U, H, wl.d_v))
     beta = None
-    if wl.has_beta:
+    if wl.variant == GDN2:
+        beta = _sigmoid(rng.standard_normal((U, H, wl.d_k + wl.d_v))).astype(np.float32)
+    elif wl.has_beta:
         beta = _sigmoid(rng.standard_normal((U, H))).astype(np.float32)
     dshape = (U, H, wl.d_k) if wl.channel_decay else (U, H)
     x = wl.decay_mean + wl.decay_std * rng.standard_normal(dshape)

@@ -107,7 +107,7 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
                 v_sel.append(s.v_f32.reshape(P, -1)[sel])
                 g_sel.append(s.g.reshape(P, -1)[sel] if wl.channel_decay else s.g.reshape(P)[sel])
                 if s.beta is not None:
-                    b_sel.append(s.beta.reshape(P)[sel])
+                    b_sel.append(s.beta.reshape((P,) if wl.beta_width == 1 else (P, -1))[sel])
             for path in paths:
                 o_full = torch.zeros((wl.units_total, H, d), dtype=torch.float32, device="cuda")
                 for l in range(layers):

@@ -53,11 +53,14 @@ def _expected_bytes(variant, units, heads, d, L, es, form=B.DL_LOG_WY):
 
 
 @pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS])
-@pytest.mark.parametrize("variant", [B.DL_GDN, B.DL_KDA, B.DL_RWKV6])
+@pytest.mark.parametrize("variant", [B.DL_GDN, B.DL_KDA, B.DL_RWKV6, B.DL_GDN2])
 @pytest.mark.parametrize("d,L,dt,es", [(128, 16, B.DL_BF16, 2), (64, 32, B.DL_F32, 4),
                                        (128, 0, B.DL_BF16, 2), (64, 64, B.DL_BF16, 2)])
 def test_state_bytes(variant, d, L, dt, es, form):
     desc = B.DlDesc(variant, 7, 3, d, d, L, dt, 0, form)
+    if variant == B.DL_GDN2 and form == B.DL_LOG_WY and L > 0:
+        assert B.dl_state_bytes(desc) == 0          # not built: factor form only
+        return
     assert B.dl_state_bytes(desc) == _expected_bytes(variant, 7, 3, d, L, es, form)
 
 
@@ -70,7 +73,6 @@ def test_state_bytes_full_size_configs():
 
 
 @pytest.mark.parametrize("fields,code", [
-    ((3, 4, 2, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),      # unknown variant
     ((0, 0, 2, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),      # no units
     ((0, 4, 0, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),      # no heads
     ((0, 4, 2, 128, 128, 8, 7), B.DL_ERR_INVALID),              # unknown dtype
@@ -80,6 +82,8 @@ def test_state_bytes_full_size_configs():
     ((0, 4, 2, 128, 128, 65, B.DL_BF16), B.DL_ERR_UNSUPPORTED), # L too long
     ((0, 4, 2, 128, 128, 8, B.DL_BF16, 2), B.DL_ERR_INVALID),   # merge_on_step not 0 / 1
     ((0, 4, 2, 128, 128, 8, B.DL_BF16, 0, 2), B.DL_ERR_INVALID),  # unknown log form
+    ((4, 4, 2, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),        # unknown variant
+    ((3, 4, 2, 128, 128, 8, B.DL_BF16, 0, 0), B.DL_ERR_UNSUPPORTED),  # gated log in WY form
 ])
 def test_bad_descriptors(lib, fields, code):
     desc = B.DlDesc(*fields)

@@ -18,6 +18,11 @@ from gpu_harness import assert_parity, log, run_case
 pytestmark = pytest.mark.gpu
 
 PATHS = ("eager", "log", "log-replay", "log-fused", "af", "af-fused")
+GATED_PATHS = ("eager", "af", "af-fused")     # the gated form's log is the factor form
+
+
+def _paths(wl):
+    return GATED_PATHS if wl.variant == W.GDN2 else PATHS
 
 
 def test_tiny_gdn_full_config():
@@ -49,6 +54,12 @@ SCALED = [
     (W.RWKV6_ADD.scaled(dtype="f32", batch=2, heads=2, steps=50), 7),
     # fp32 keys with per-channel decay and L = 64 stage 65.5 KiB of LDS (> 64 KiB)
     (W.KDA_SWEEP.scaled(dtype="f32", batch=1, heads=2, steps=70), 64),
+    # the gated form (channel-wise erase and write gates)
+    (W.GATED.scaled(batch=3, heads=3, steps=70), 16),
+    (W.GATED.scaled(batch=2, heads=3, steps=45), 1),
+    (W.GATED.scaled(batch=2, heads=2, steps=75), 32),
+    (W.GATED.scaled(batch=2, heads=2, steps=140), 64),
+    (W.GATED.scaled(d_k=64, d_v=64, dtype="f32", batch=2, heads=2, steps=40), 7),
 ]
 
 
@@ -56,7 +67,7 @@ SCALED = [
                                              for w, L in SCALED])
 def test_scaled_parity(wl, L):
     log(f"case {wl.name} variant={wl.variant} dtype={wl.dtype} d={wl.d_k} L={L} T={wl.steps}")
-    assert_parity(run_case(wl, L, PATHS), label=f"{wl.name} L={L}")
+    assert_parity(run_case(wl, L, _paths(wl)), label=f"{wl.name} L={L}")
 
 
 def test_merge_every_step_is_a_no_op_until_full():

@@ -231,7 +231,7 @@ def main(argv=None):
         n_cal = 4
         qc = rng.standard_normal((16, n_cal, d)).astype(np.float32)
         gc = -np.abs(rng.standard_normal((16, n_cal, d) if wl.channel_decay else (16, n_cal))).astype(np.float32)
-        bc = rng.random((16, n_cal)).astype(np.float32)
+        bc = rng.random((16, n_cal) if wl.beta_width == 1 else (16, n_cal, wl.beta_width)).astype(np.float32)
         tc = time.time()
         oracle.run(wl.variant, qc, qc, qc, gc, bc, threads=1)
         per_core = 16 * n_cal / max(time.time() - tc, 1e-6)

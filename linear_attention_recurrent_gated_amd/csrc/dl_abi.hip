@@ -220,9 +220,16 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.flags = reinterpret_cast<int *>(m + l.off_flags);
     p.fuse = desc->merge_on_step;
     p.af = factors_form(*desc) ? 1 : 0;
-    // stream the state when the base is larger than MI355X's 256 MiB Infinity
-    // Cache: such a state set cannot stay resident between calls
-    p.stream = (size_t)desc->units * desc->heads * desc->d_v * desc->d_k * 4 > ((size_t)256 << 20);
+    // Stream the state (nontemporal loads and stores) when what the steps
+    // re-read does not fit MI355X's 256 MiB Infinity Cache.  Eager: the state
+    // itself.  With a log, every step reads the whole base and the logged
+    // entries; once base and log together are well past the cache (1.5x),
+    // streaming the base keeps the log entries, read back by every step,
+    // resident instead of letting both thrash.
+    const size_t base_bytes = (size_t)desc->units * desc->heads * desc->d_v * desc->d_k * 4;
+    const size_t log_bytes = l.total - l.off_k;
+    p.stream = desc->log_len == 0 ? base_bytes > ((size_t)256 << 20)
+                                  : base_bytes + log_bytes > ((size_t)384 << 20);
     p.fill = reinterpret_cast<int *>(m + l.off_fill);
     p.base = reinterpret_cast<float *>(m + l.off_base);
     const bool has_log = desc->log_len > 0;

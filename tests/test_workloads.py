@@ -26,7 +26,7 @@ def test_bf16_rounding_matches_torch():
     assert np.array_equal(back, ref_back)
 
 
-@pytest.mark.parametrize("cfg_id", [1, 2, 3, 5])
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 5, 6])
 def test_step_shapes_and_norms(cfg_id):
     wl = W.WORKLOADS[cfg_id].scaled(batch=4)
     s = W.draw_step(wl, 3, seed=0)
@@ -35,6 +35,8 @@ def test_step_shapes_and_norms(cfg_id):
     assert s.g.dtype == np.float32
     assert s.g.shape == ((U, H, wl.d_k) if wl.channel_decay else (U, H))
     assert (s.beta is None) == (not wl.has_beta)
+    if s.beta is not None:
+        assert s.beta.shape == ((U, H) if wl.beta_width == 1 else (U, H, wl.d_k + wl.d_v))
     if wl.dtype == "bf16":
         assert s.q.dtype == np.uint16
         assert np.array_equal(W.bf16_bits_to_f32(s.q), s.q_f32)
@@ -69,7 +71,7 @@ def _mean_of(f, mu, sd):
     return val
 
 
-@pytest.mark.parametrize("cfg_id", [2, 3, 5])
+@pytest.mark.parametrize("cfg_id", [2, 3, 5, 6])
 def test_decay_and_beta_distributions(cfg_id):
     wl = W.WORKLOADS[cfg_id].scaled(batch=16)
     s = W.draw_step(wl, 0, 0)

@@ -123,17 +123,22 @@ def test_null_handle_is_rejected(lib):
 
 @pytest.mark.parametrize("variant,d,dt,fuse", [(B.DL_GDN, 128, B.DL_BF16, 1), (B.DL_KDA, 128, B.DL_BF16, 1),
                                                (B.DL_KDA, 128, B.DL_BF16, 0), (B.DL_RWKV6, 64, B.DL_BF16, 0),
-                                               (B.DL_GDN, 64, B.DL_F32, 0)])
+                                               (B.DL_GDN, 64, B.DL_F32, 0), (B.DL_GDN2, 128, B.DL_BF16, 1)])
 @pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS])
 def test_suggest_log_len(lib, variant, d, dt, fuse, form):
     """The suggested L is the argmin of the documented traffic model, and its
     modeled bytes undercut both extremes (merge every step, longest log)."""
     desc = B.DlDesc(variant, 1, 1, d, d, 0, dt, fuse, form)
+    if variant == B.DL_GDN2 and form == B.DL_LOG_WY:
+        with pytest.raises(B.DlError):            # the gated log exists in the factor form only
+            B.dl_suggest_log_len(desc)
+        return
     L, b = B.dl_suggest_log_len(desc)
     assert 1 < L < 64
     es = 2 if dt == B.DL_BF16 else 4
     af = form == B.DL_LOG_FACTORS and variant != B.DL_RWKV6
-    St, g, bb = 4 * d * d, (4 if variant == B.DL_GDN else 4 * d), (0 if variant == B.DL_RWKV6 else 4)
+    St, g = 4 * d * d, (4 if variant == B.DL_GDN else 4 * d)
+    bb = 0 if variant == B.DL_RWKV6 else (8 * d if variant == B.DL_GDN2 else 4)
     In, Out = 3 * d * es + g + bb, 4 * d
     E = d * es + d * (4 if af else es) + g + (0 if af else bb)
 

@@ -71,11 +71,15 @@ def eager_bytes(m):
     return 2 * m["St"] + m["In"] + m["Out"] + 4
 
 
-def log_step_bytes(m, c_prev):
+def log_step_bytes(m, c_prev, merges=False):
     """Per state with c_prev logged entries: read S0 and the logged entries,
     read inputs, append one entry, write o, read and write the fill counter;
     delta-rule variants also read the c_prev (c_prev - 1) / 2 stored
-    key-side factors and write the new entry's c_prev."""
+    key-side factors and write the new entry's c_prev.  A step that merges
+    in place writes the new base instead of appending the entry."""
+    if merges:
+        r = m["R"] * 4 * (c_prev * (c_prev - 1) // 2)
+        return m["St"] + c_prev * m["E"] + m["In"] + m["Out"] + 8 + r + m["St"]
     r = m["R"] * 4 * (c_prev * (c_prev - 1) // 2 + c_prev)
     return m["St"] + c_prev * m["E"] + m["In"] + m["E"] + m["Out"] + 8 + r
 
@@ -404,7 +408,7 @@ def main(argv=None):
                 for l in range(layers):
                     if fused:
                         # the step that fills a log also writes the merged base
-                        step_bytes.append(float(np.sum([log_step_bytes(m, c) + (m["St"] if c == L - 1 else 0)
+                        step_bytes.append(float(np.sum([log_step_bytes(m, c, merges=c == L - 1)
                                                         for c in f])) * H)
                     else:
                         step_bytes.append(float(np.sum([log_step_bytes(m, c) for c in f])) * H)

@@ -113,7 +113,8 @@ typedef struct {
     int32_t in_dtype;  /* dl_dtype of q, k, v and of the logged k, v copies */
     int32_t merge_on_step; /* 0: a full log waits for dl_merge; 1: the log step
                             * that fills a log also merges it into the base in
-                            * the same pass and leaves fill at 0 */
+                            * the same pass and leaves fill at 0 (that entry
+                            * is not written to the log) */
     int32_t log_form;  /* dl_log_form */
 } dl_desc;
 
@@ -240,11 +241,12 @@ int32_t dl_version(void);
 
 /* Log length with the lowest modeled cost per state update for the shape in
  * `desc` (variant, d_k, d_v, in_dtype, merge_on_step, log_form;
- * desc->log_len and the unit and head counts are ignored).  The model is the traffic the method
- * must move per update -- the base read, the logged entries read back, the
- * append, the key-side factors and the amortised merge (one base write per L
- * steps when merge_on_step is set, else a separate read + write of the base
- * and the log) -- divided by the share of its bandwidth-bound rate the step
+ * desc->log_len and the unit and head counts are ignored).  The model is the
+ * traffic the method must move per update -- the base read, the logged
+ * entries read back, the append, the key-side factors and the amortised merge
+ * (one base write per L steps, in place of that step's append, when
+ * merge_on_step is set, else a separate read + write of the base and the
+ * log) -- divided by the share of its bandwidth-bound rate the step
  * kernel keeps at that L: it needs four workgroups per CU, and fewer fit once
  * the staged log outgrows a quarter of the CU's 160 KiB LDS.  This is the
  * merge-interval trade-off of the DeltaLog page's Traffic Model, made

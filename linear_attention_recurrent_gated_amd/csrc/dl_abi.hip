@@ -413,7 +413,9 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
         const double c = (L - 1) / 2.0;                           // mean logged entries read
         const double rt = delta ? 4.0 * ((L - 1.0) * (L - 2.0) / 6.0 + c) : 0.0;
         double bytes = St + c * E + E + In + Out + 8.0 + rt;
-        bytes += fuse ? St / L : (2.0 * St + L * E + 8.0) / L;
+        // merging in place writes the base once per L steps and saves that
+        // step's append; a separate merge reads and writes the base and reads the log
+        bytes += fuse ? (St - E) / L : (2.0 * St + L * E + 8.0) / L;
         const int lds = af ? dl::af_plan(d.d_k, L, fuse).bytes
                            : dl::step_plan(d.variant, d.d_k, (int)es, L, fuse).bytes;
         const int wgs = std::min(4, (160 * 1024) / std::max(lds, 1));

@@ -747,14 +747,16 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
             orow[row] = acc_o;
     }
     if constexpr (APPEND) {
-        if (wave == 0)
-            log_append<V, D, T>(P, pair, n, smem, sp, lane);
         if constexpr (FUSE) {
+            // the entry that fills the log goes straight into the merged base;
+            // the emptied log keeps no copy of it
             if (n == L - 1) {
                 merge_in_step<V, D, T, MV, NT>(P, pair, ct, smem, sp, st, vc, lam_c);
                 return;
             }
         }
+        if (wave == 0)
+            log_append<V, D, T>(P, pair, n, smem, sp, lane);
         if (tid == 0)
             P.fill[pair] = n + 1;
     }

@@ -435,7 +435,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
                                  ? reinterpret_cast<const float *>(smem + ap.off_w)[row] * vr - ax
                                  : b_in * (vr - ax);
             ao += rn * an;
-            if (s == 1)
+            if (s == 1 && !merging)
                 alog[row] = an;
             if (FUSE && merging && s == 0)
                 sa[n * D + row] = an;
@@ -444,8 +444,10 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
             orow[row] = ao;
     }
     if constexpr (APPEND) {
-        // the rest of entry n: the key (bit copy) and Lam_n
-        if (wave == 0) {
+        // the rest of entry n: the key (bit copy) and Lam_n (not for the entry
+        // that fills the log when it merges in place: it goes straight into
+        // the merged base and the emptied log keeps no copy of it)
+        if (wave == 0 && !merging) {
             if (ro == 0) {
                 uint4 *dst = reinterpret_cast<uint4 *>(static_cast<T *>(P.log_k) + (e0 + n) * D + ch0);
                 dst[0] = kr.a;

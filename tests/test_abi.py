@@ -146,7 +146,7 @@ def test_suggest_log_len(lib, variant, d, dt, fuse, form):
         c = (L - 1) / 2
         rt = 4 * ((L - 1) * (L - 2) / 6 + c) if variant != B.DL_RWKV6 and not af else 0
         x = St + c * E + E + In + Out + 8 + rt
-        return x + (St / L if fuse else (2 * St + L * E + 8) / L)
+        return x + ((St - E) / L if fuse else (2 * St + L * E + 8) / L)
 
     assert b == pytest.approx(model(L), rel=1e-12)
     assert b < model(1) and b < model(64)

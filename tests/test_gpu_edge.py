@@ -56,8 +56,8 @@ def test_schedule_and_payload_bit_exact(wl, L, path):
             m = tau - first[b] + 1                      # tokens this sequence has taken
             expect = max(m, 0) % L
             assert np.all(fill[b] == expect), (tau, b, fill[b], expect)
-            if m <= 0:
-                continue
+            if m <= 0 or (path.endswith("-fused") and m % L == 0):
+                continue                                # merged in place: no entry kept
             slot = (m - 1) % L
             assert np.array_equal(_bits(st.log_k[b, :, slot]), _bits(to_torch(s.k[b], wl.dtype)))
             assert np.array_equal(_bits(st.log_v[b, :, slot]), _bits(to_torch(s.v[b], wl.dtype)))
@@ -113,8 +113,8 @@ def test_factor_log_payload(wl, L, path):
         for b in range(wl.batch):
             m = tau - first[b] + 1
             assert np.all(fill[b] == max(m, 0) % L), (tau, b, fill[b])
-            if m <= 0:
-                continue
+            if m <= 0 or (path.endswith("-fused") and m % L == 0):
+                continue                                # merged in place: no entry kept
             slot = (m - 1) % L
             assert np.array_equal(_bits(st.log_k[b, :, slot]), _bits(to_torch(s.k[b], wl.dtype)))
             lam = np.zeros_like(s.g[b])

@@ -2,21 +2,27 @@
 """Decode-time recurrent-state update benchmark on one MI355X: eager vs DeltaLog.
 
 A step is one decode token for every (sequence, layer, head) state of the
-workload: the DeltaLog path appends to the log and reads out from the
-read-only base (dl_decode_step_log), merging full logs into the base in WY
-form (dl_merge); the eager path rewrites every state (dl_decode_step_eager).
+workload: a DeltaLog path appends to the log and reads out from the
+read-only base (dl_decode_step_log) and merges full logs into the base --
+with a separate launch (dl_merge) or inside the step that fills them
+(merge_on_step) -- keeping either the compact-WY log or the additive-factor
+log (log_form); the eager path rewrites every state (dl_decode_step_eager).
 Inputs for all steps are resident in HBM before timing starts.  One JSON
 line is printed:
 
-  value          DeltaLog state updates/s (one update = one state, one token)
-  roofline       the DeltaLog step kernel's algorithmic bytes per launch over
-                 its average HIP-event duration, against 8 TB/s
+  value          the fastest DeltaLog path's state updates/s (one update =
+                 one state, one token); its name is in "path"
+  roofline       that path's step kernel: algorithmic bytes per launch over
+                 its average HIP-event duration, against 8 TB/s, and the
+                 counter-measured bytes per launch ("traffic") when the
+                 committed profile matches the sources
   eager          the same for the eager path
-  merge          the merge kernel's bytes and MFMA rate
+  other_paths    the same for the other DeltaLog paths
+  merge          the separate merge kernels' bytes and fp32 rate
   cpu_baseline   the float64 oracle on the host cores, on a bounded sample
   parity         the sampled GPU outputs and final states against the oracle
 
-Usage: python bench.py [--config 1..5] [--L n] [--steps K] [--warmup W]
+Usage: python bench.py [--config 1..6] [--L n] [--steps K] [--warmup W] [--paths ...]
 """
 from __future__ import annotations
 

@@ -1,4 +1,5 @@
-// Additive-factor DeltaLog for the delta-rule operators (GDN, KDA) on gfx950.
+// Additive-factor DeltaLog for the delta-rule operators (GDN, KDA and the
+// gated form) on gfx950.
 //
 // The log holds the compact update factors (a_j, b_j = k_j) of each pending
 // step with its log-decay snapshot Lam_j (the DeltaLog page, "DeltaLog:
@@ -30,9 +31,10 @@
 // four waves per (row, head), S0 rows in registers (lane groups of 8, lane s
 // holding the columns 4s + 32m + e).  Each logged key and decay is used by
 // exactly one lane (the dot products above, eight channels per lane), so that
-// lane loads it straight from the log -- the first two passes of entries are
-// in flight with S0 -- and only the factors a_j, which every lane group of a
-// row reads, are staged in LDS (direct-to-LDS loads).
+// lane loads it straight from the log into registers -- the first pass (two
+// for head-wise decay) in flight with S0, the rest issued right after the
+// first barrier -- and only the factors a_j, which every lane group of a row
+// reads, are staged in LDS (direct-to-LDS loads).
 #include "dl_common.hpp"
 
 namespace dl {

@@ -85,3 +85,34 @@ def test_determinism_bitwise():
     for path in PATHS:
         assert np.array_equal(a.gpu[path][0], b.gpu[path][0]), path
         assert np.array_equal(a.gpu[path][1], b.gpu[path][1]), path
+
+
+def _random_cases(n=14, seed=2024):
+    """Seeded draws over the built shapes: variant, d, dtype, L, batch, heads,
+    steps (ragged tails included) and ragged log offsets."""
+    rng = np.random.default_rng(seed)
+    bases = [W.GDN_HYBRID, W.KDA_SWEEP, W.RWKV6_ADD, W.GATED]
+    out = []
+    for i in range(n):
+        base = bases[i % len(bases)]
+        d = int(rng.choice([64, 128]))
+        L = int(rng.choice([1, 2, 5, 8, 13, 16, 24, 32, 47, 64]))
+        steps = int(rng.integers(L // 2 + 1, 2 * L + 9))
+        wl = base.scaled(name=f"{base.name}-rand{i}", d_k=d, d_v=d,
+                         dtype=str(rng.choice(["bf16", "f32"])),
+                         batch=int(rng.integers(1, 4)), heads=int(rng.integers(1, 4)),
+                         steps=steps, ragged=bool(rng.random() < 0.4),
+                         state_std=float(rng.choice([0.0, 0.02, 0.5])))
+        out.append((wl, L))
+    return out
+
+
+RANDOM = _random_cases()
+
+
+@pytest.mark.parametrize("wl,L", RANDOM, ids=[f"{w.name}-{w.variant}-{w.dtype}-d{w.d_k}-L{L}-T{w.steps}"
+                                             f"{'-ragged' if w.ragged else ''}" for w, L in RANDOM])
+def test_random_shapes_parity(wl, L):
+    log(f"case {wl.name} variant={wl.variant} dtype={wl.dtype} d={wl.d_k} L={L} T={wl.steps} "
+        f"ragged={wl.ragged} std={wl.state_std}")
+    assert_parity(run_case(wl, L, _paths(wl)), label=f"{wl.name} L={L}")

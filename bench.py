@@ -527,6 +527,14 @@ def main(argv=None):
                            if ms else None}
     if merges:
         out["merge"] = merges
+    if main_path in knames:
+        # the log length the traffic model suggests for this shape, form and schedule
+        sdesc = B.DlDesc(wl.variant, 1, 1, wl.d_k, wl.d_v, 0,
+                         B.DL_BF16 if wl.dtype == "bf16" else B.DL_F32,
+                         int(main_path.endswith("-fused")),
+                         B.DL_LOG_FACTORS if main_path.startswith("af") else B.DL_LOG_WY)
+        sL, sbytes = B.dl_suggest_log_len(sdesc)
+        out["suggested_log_len"] = {"path": main_path, "L": sL, "modeled_bytes_per_update": sbytes}
 
     # ---- the oracle on the host cores, same inputs, sampled states
     if not args.no_cpu_baseline:

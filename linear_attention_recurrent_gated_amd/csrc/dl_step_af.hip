@@ -407,7 +407,9 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
         cr[mm] = j < n ? sr[jc] : 0.f;
         cu[mm] = (APPEND && j < n) ? su[jc] : 0.f;
     }
-    const float rn = APPEND ? sr[n] : 0.f;      // r_n = k . q (D(n, n) = 1)
+    // r_n = k . q (D(n, n) = 1), the same for the whole workgroup: kept in a
+    // scalar register
+    const float rn = APPEND ? __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(sr[n]))) : 0.f;
     float *alog = static_cast<float *>(P.log_v) + (e0 + n) * D;
 #pragma unroll
     for (int it = 0; it < SH::ITER; ++it) {

@@ -205,6 +205,7 @@ struct StepPlan {
     int off_qin;   // q as floats, D
     int off_q;     // q0, D floats
     int off_y;     // merge in the step: 16 rows of Y = R Q, D floats each
+                   // (in the staged values' place when they are large enough)
     int bytes;
 };
 
@@ -264,8 +265,11 @@ __host__ __device__ inline StepPlan step_plan(int variant, int D, int esize, int
     p.off_e = p.off_c + 4 * 256;
     p.off_qin = p.off_e + 4 * 256;
     p.off_q = p.off_qin + D * 4;
-    p.off_y = p.off_q + D * 4;
-    p.bytes = p.off_y + (fuse ? 16 * D * 4 : 0);
+    // Y is built after the merge has read every logged value, so it can take
+    // the staged values' place when they span at least 16 rows of D floats
+    const bool y_in_v = round_up(L * D * esize, 1024) >= 16 * D * 4;
+    p.off_y = y_in_v ? p.off_v : p.off_q + D * 4;
+    p.bytes = p.off_q + D * 4 + ((fuse && !y_in_v) ? 16 * D * 4 : 0);
     return p;
 }
 

@@ -331,7 +331,9 @@ __device__ __forceinline__ void merge_in_step(const Params &P, size_t pair, int 
 #pragma unroll
             for (int u = 0; u < JPT; ++u)
                 acc[u] = 0.f;
-            for (int i = jb; i < ct; ++i) {
+            // the additive variant has R = I: only i = j contributes
+            const int iend = (V == RWKV6) ? (jb + JPT < ct ? jb + JPT : ct) : ct;
+            for (int i = jb; i < iend; ++i) {
                 float qi = sf[i] * Elem<T>::load1(reinterpret_cast<const T *>(krow(i)) + ych);
                 if constexpr (V != GDN)
                     qi *= fast_exp(lc_y - slam[i * D + ych]);

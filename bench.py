@@ -111,8 +111,9 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from a committed counter summary, if it matches the sources."""
+def counter_traffic(kernel: str, workload: str, log_len: int | None = None):
+    """HBM bytes per launch from a committed counter summary, if it matches the
+    sources and, for a log kernel, the log length it was taken at."""
     path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.md")
     if not os.path.exists(path):
         return None
@@ -123,6 +124,8 @@ def counter_traffic(kernel: str, workload: str):
                 k, v = line[2:].split(":", 1)
                 vals[k.strip()] = v.strip().strip("`")
     if vals.get("source_sha256_16") != source_hash():
+        return None
+    if log_len is not None and vals.get("log_len") not in (None, str(log_len)):
         return None
     try:
         return float(vals["traffic_bytes_per_launch"])
@@ -505,7 +508,7 @@ def main(argv=None):
                        "frac": r["step_kernel_GBps"] / HBM_PEAK_GBPS,
                        "avg_launch_us": r["step_kernel_avg_us"],
                        "algorithmic_bytes_per_launch": r["step_bytes_per_launch"],
-                       "traffic": counter_traffic(kname, wl.name)}
+                       "traffic": counter_traffic(kname, wl.name, L)}
     if "eager" in results and main_path != "eager":
         e = results["eager"]
         out["eager"] = {"value": e["updates_per_s"], "ms_per_step": e["ms_per_step"],
@@ -530,7 +533,7 @@ def main(argv=None):
                        "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS,
                        "avg_launch_us": u["step_kernel_avg_us"],
                        "algorithmic_bytes_per_launch": u["step_bytes_per_launch"],
-                       "traffic": counter_traffic(kn, wl.name)})
+                       "traffic": counter_traffic(kn, wl.name, L)})
     if others:
         out["other_paths"] = others
     merges = {}

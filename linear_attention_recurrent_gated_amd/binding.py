@@ -237,32 +237,43 @@ class DecodeState:
             return self.torch.cuda.current_stream().cuda_stream
         return getattr(stream, "cuda_stream", stream)
 
+    def _tensor(self, name, x, dtype, shape):
+        """Raise ValueError unless ``x`` is a contiguous ``dtype`` tensor of
+        ``shape`` on this state's device (the library sees raw pointers only)."""
+        if x is None:
+            raise ValueError(f"{name} is required")
+        if x.dtype != dtype or tuple(x.shape) != tuple(shape) or not x.is_contiguous() \
+                or x.device != self.buf.device:
+            raise ValueError(f"{name}: expected a contiguous {dtype} tensor of shape {tuple(shape)} "
+                             f"on {self.buf.device}, got {x.dtype} {tuple(x.shape)} on {x.device}"
+                             f"{'' if x.is_contiguous() else ' (not contiguous)'}")
+        return x
+
+    def _slots(self, slot_idx, rows):
+        if slot_idx is None:
+            return None
+        return self._tensor("slot_idx", slot_idx, self.torch.int32, (rows,)).data_ptr()
+
     def _rows(self, q, slot_idx):
         rows = q.shape[0]
-        sp = None
-        if slot_idx is not None:
-            assert slot_idx.dtype == self.torch.int32 and slot_idx.is_cuda and slot_idx.is_contiguous()
-            assert slot_idx.shape == (rows,)
-            sp = slot_idx.data_ptr()
-        return rows, sp
+        self._tensor("q", q, self.in_torch_dtype, (rows, self.heads, self.d))
+        return rows, self._slots(slot_idx, rows)
 
     def _check_inputs(self, rows, q, k, v, g, beta):
         t = self.torch
         H, d = self.heads, self.d
-        for x in (q, k, v):
-            assert x.dtype == self.in_torch_dtype and x.is_contiguous() and x.shape == (rows, H, d)
-        gshape = (rows, H) if self.variant == DL_GDN else (rows, H, d)
-        assert g.dtype == t.float32 and g.is_contiguous() and tuple(g.shape) == gshape
+        for name, x in (("q", q), ("k", k), ("v", v)):
+            self._tensor(name, x, self.in_torch_dtype, (rows, H, d))
+        self._tensor("g", g, t.float32, (rows, H) if self.variant == DL_GDN else (rows, H, d))
         if self.variant != DL_RWKV6:
-            bshape = (rows, H, 2 * d) if self.variant == DL_GDN2 else (rows, H)
-            assert beta.dtype == t.float32 and beta.is_contiguous() and tuple(beta.shape) == bshape
+            self._tensor("beta", beta, t.float32,
+                         (rows, H, 2 * d) if self.variant == DL_GDN2 else (rows, H))
 
     def _out(self, rows, o):
         if o is None:
-            o = self.torch.empty((rows, self.heads, self.d), dtype=self.torch.float32,
-                                 device=self.buf.device)
-        assert o.dtype == self.torch.float32 and o.is_contiguous()
-        return o
+            return self.torch.empty((rows, self.heads, self.d), dtype=self.torch.float32,
+                                    device=self.buf.device)
+        return self._tensor("o", o, self.torch.float32, (rows, self.heads, self.d))
 
     def step_eager(self, q, k, v, g, beta=None, o=None, slot_idx=None, stream=None):
         rows, sp = self._rows(q, slot_idx)
@@ -286,13 +297,12 @@ class DecodeState:
               replay: bool = False, stream=None):
         if rows is None:
             rows = self.units if slot_idx is None else slot_idx.shape[0]
-        sp = None if slot_idx is None else slot_idx.data_ptr()
+        sp = self._slots(slot_idx, rows)
         fn = dl_merge_replay if replay else dl_merge
         fn(self.handle, rows, sp, mode, self._stream(stream))
 
     def readout(self, q, o=None, slot_idx=None, stream=None):
         rows, sp = self._rows(q, slot_idx)
-        assert q.dtype == self.in_torch_dtype and q.is_contiguous()
         o = self._out(rows, o)
         dl_readout(self.handle, rows, sp, q.data_ptr(), o.data_ptr(), self._stream(stream))
         return o

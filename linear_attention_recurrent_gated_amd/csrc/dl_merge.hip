@@ -131,8 +131,8 @@ __global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *
 // the key-side phases so they overlap them.
 // ---------------------------------------------------------------------------
 template <int V, int D, typename T, bool NT>
-__global__ void __launch_bounds__(256) merge_wy_kernel(Params P, const int *__restrict__ slot_idx,
-                                                       int mode) {
+__global__ void __launch_bounds__(256, (V == KDA && D == 128) ? 3 : 1)
+merge_wy_kernel(Params P, const int *__restrict__ slot_idx, int mode) {
     constexpr int C = 16;               // entries per WY chunk
     constexpr int NIT = D / 64;         // 16-row value tiles per wave
     constexpr int NM = D / 16;          // 16-column blocks

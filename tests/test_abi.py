@@ -155,3 +155,34 @@ def test_suggest_log_len(lib, variant, d, dt, fuse, form):
 def test_suggest_log_len_errors(lib):
     with pytest.raises(B.DlError):
         B.dl_suggest_log_len(B.DlDesc(0, 1, 1, 96, 96, 0, B.DL_BF16))
+
+
+def test_binding_rejects_bad_tensors():
+    """The torch wrapper checks dtype, shape, layout and device before passing
+    raw pointers on (the library cannot see shapes)."""
+    import torch
+    st = B.DecodeState.__new__(B.DecodeState)     # host logic only: no state block
+    st.torch, st.buf = torch, torch.empty(0, dtype=torch.uint8)
+    st.heads, st.d, st.variant, st.in_torch_dtype = 2, 64, B.DL_GDN, torch.float32
+    x, g, b = torch.zeros(3, 2, 64), torch.zeros(3, 2), torch.zeros(3, 2)
+    st._check_inputs(3, x, x, x, g, b)
+    assert st._out(3, None).shape == (3, 2, 64)
+    bad = (torch.zeros(3, 2, 32), torch.zeros(3, 2, 64, dtype=torch.float64),
+           torch.zeros(3, 64, 2).transpose(1, 2))
+    for y in bad:
+        with pytest.raises(ValueError):
+            st._check_inputs(3, x, y, x, g, b)
+        with pytest.raises(ValueError):
+            st._out(3, y)
+    with pytest.raises(ValueError):
+        st._check_inputs(3, x, x, x, torch.zeros(3, 2, 64), b)   # GDN decay is one scalar per head
+    with pytest.raises(ValueError):
+        st._check_inputs(3, x, x, x, g, None)                    # beta is required
+    st.variant = B.DL_GDN2
+    with pytest.raises(ValueError):
+        st._check_inputs(3, x, x, x, torch.zeros(3, 2, 64), b)   # gated: [rows, H, d_k + d_v]
+    st._check_inputs(3, x, x, x, torch.zeros(3, 2, 64), torch.zeros(3, 2, 128))
+    with pytest.raises(ValueError):
+        st._slots(torch.zeros(3, dtype=torch.int64), 3)
+    with pytest.raises(ValueError):
+        st._slots(torch.zeros(4, dtype=torch.int32), 3)

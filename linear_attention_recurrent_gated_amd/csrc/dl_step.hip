@@ -103,6 +103,11 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
         reject_row(P, orow, D, DL_FLAG_LOG_NONEMPTY);
         return;
     }
+    // The gated form scales this lane's state columns by alpha once, in
+    // place: its row dots and update then read S diag(alpha), and the decay
+    // vector is dead before the row loop.  (The other per-key-decay
+    // variants measured faster folding alpha into the key and query.)
+    constexpr bool FOLD = V == GDN2;
     float alpha = 1.f;
     if constexpr (V == GDN) {
         alpha = expf(g_s);
@@ -111,15 +116,27 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
         for (int f = 0; f < SH::FPL; ++f)
             ac[f] = expf(ac[f]);
     }
+    if constexpr (FOLD) {
+#pragma unroll
+        for (int it = 0; it < SH::ITER; ++it) {
+#pragma unroll
+            for (int m = 0; m < SH::NCH; ++m) {
+                st[it][m].x *= ac[4 * m];
+                st[it][m].y *= ac[4 * m + 1];
+                st[it][m].z *= ac[4 * m + 2];
+                st[it][m].w *= ac[4 * m + 3];
+            }
+        }
+    }
 
-    // k.q, and the decayed key / query the row dots use
+    // k.q, and the key / query the row dots read
     float kq = 0.f;
     float ak[SH::FPL], aq[SH::FPL];
 #pragma unroll
     for (int f = 0; f < SH::FPL; ++f) {
         kq += kc[f] * qc[f];
-        ak[f] = (V == GDN) ? kc[f] : (V == GDN2) ? ac[f] * ec[f] * kc[f] : ac[f] * kc[f];
-        aq[f] = (V == GDN) ? qc[f] : ac[f] * qc[f];
+        ak[f] = (V == GDN) ? kc[f] : (V == GDN2) ? ec[f] * kc[f] : ac[f] * kc[f];
+        aq[f] = (V == GDN || FOLD) ? qc[f] : ac[f] * qc[f];
     }
     kq = sum8(kq);
 
@@ -149,7 +166,7 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int f = 4 * m + e;
-                const float decayed = (V == GDN) ? alpha * sv[e] : sv[e] * ac[f];
+                const float decayed = (V == GDN) ? alpha * sv[e] : FOLD ? sv[e] : sv[e] * ac[f];
                 sv[e] = decayed + d * kc[f];
             }
             store_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0), make_float4(sv[0], sv[1], sv[2], sv[3]));

@@ -188,9 +188,14 @@ dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_i
  * o = S_logical q from the read-only base plus the log, the new entry
  * included.  Under DL_LOG_FACTORS the entry is (a_t, k_t, the decay), with
  * a_t read from base + log in the same pass; the readout is then base
- * (E q) plus one independent dot product per entry.  When the log now holds L entries it is full: call dl_merge
- * (DL_MERGE_FULL) before the unit's next step, or that step is skipped with
- * DL_FLAG_LOG_FULL.  Arguments as for dl_decode_step_eager; needs L >= 1. */
+ * (E q) plus one independent dot product per entry.  When the log now holds
+ * L entries it is full: call dl_merge (DL_MERGE_FULL) before the unit's next
+ * step, or that step is skipped with DL_FLAG_LOG_FULL.  Arguments as for
+ * dl_decode_step_eager; needs L >= 1.  g must be finite: the log keeps the
+ * decay accumulated since its first entry (log_g) in fp32, and the decay
+ * between two entries is the exponential of a difference of those sums, so
+ * its relative rounding error is about 6e-8 times the sum's magnitude (1e-5
+ * at a sum of -170 over one log). */
 dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx,
                              const void *q, const void *k, const void *v, const float *g,
                              const float *beta, float *o, void *stream);

@@ -272,3 +272,70 @@ def test_wy_merge_equals_replay_merge(wl, L):
     log(f"  WY vs replay {wl.name} L={L}: {err:.2e}")
     assert err <= 1e-5
     assert int(a.fill.max()) == 0 and int(b.fill.max()) == 0
+
+
+def _degenerate_inputs(variant, U, H, d, T, seed=11):
+    """fp32 inputs with one degenerate pattern per head: 0 no write (beta or
+    both gates 0), 1 no decay (g = 0), 2 a zero key every other step, 3
+    near-total forgetting (g = -30) every third step, 4 a zero query, 5 none."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, U, H, d)).astype(np.float32) / np.float32(np.sqrt(d))
+    k = rng.standard_normal((T, U, H, d)).astype(np.float32)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True).astype(np.float32)
+    v = rng.standard_normal((T, U, H, d)).astype(np.float32)
+    channel = variant != W.GDN
+    g = -rng.uniform(0.0, 1.0, (T, U, H, d) if channel else (T, U, H)).astype(np.float32)
+    width = 2 * d if variant == W.GDN2 else 1
+    beta = None if variant == W.RWKV6 else \
+        rng.uniform(0.05, 1.0, (T, U, H, width) if width > 1 else (T, U, H)).astype(np.float32)
+    if beta is not None:
+        beta[:, :, 0] = 0.0
+    g[:, :, 1] = 0.0
+    k[1::2, :, 2] = 0.0
+    g[::3, :, 3] = -30.0
+    q[:, :, 4] = 0.0
+    return q, k, v, g, beta
+
+
+@pytest.mark.parametrize("variant", [W.GDN, W.KDA, W.RWKV6, W.GDN2], ids=["gdn", "kda", "rwkv6", "gated"])
+def test_degenerate_inputs_parity(variant):
+    """No write, no decay, zero keys, near-total forgetting and zero queries
+    reach the oracle's result on every path (log tail left unmerged until the
+    final flush)."""
+    U, H, d, T, L = 2, 6, 64, 21, 8
+    q, k, v, g, beta = _degenerate_inputs(variant, U, H, d, T)
+    S0 = (0.3 * np.random.default_rng(3).standard_normal((U, H, d, d))).astype(np.float32)
+    P = U * H
+    o_ref, S_ref = oracle.run(variant, q.reshape(T, P, d), k.reshape(T, P, d), v.reshape(T, P, d),
+                              g.reshape((T, P, d) if variant != W.GDN else (T, P)),
+                              None if beta is None else beta.reshape((T, P, -1) if variant == W.GDN2 else (T, P)),
+                              S0.reshape(P, d, d), np.zeros(P, dtype=np.int64))
+    paths = ("eager", "af", "af-fused") if variant == W.GDN2 else \
+        ("eager", "log", "log-fused", "af", "af-fused")
+    for path in paths:
+        st = B.DecodeState(variant, U, H, d, 0 if path == "eager" else L, "f32",
+                           merge_on_step=path.endswith("-fused"),
+                           log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY)
+        st.base.copy_(torch.from_numpy(S0))
+        outs = []
+        for t in range(T):
+            args = tuple(None if x is None else torch.from_numpy(np.ascontiguousarray(x[t])).cuda()
+                         for x in (q, k, v, g, beta))
+            if path == "eager":
+                outs.append(st.step_eager(*args))
+            else:
+                outs.append(st.step_log(*args))
+                if (t + 1) % L == 0:
+                    st.merge(B.DL_MERGE_FULL)
+        if path != "eager":
+            st.merge(B.DL_MERGE_ALL)
+        assert st.check() == 0
+        o = torch.stack(outs, 0).double().cpu().numpy().reshape(T, P, d).transpose(1, 0, 2)
+        S = st.base.double().cpu().numpy().reshape(P, d, d)
+        eo = per_pair_error(o, o_ref.transpose(1, 0, 2))
+        eS = per_pair_error(S, S_ref)
+        log(f"  degenerate {variant} {path}: max rel err o {eo.max():.2e}, S {eS.max():.2e}")
+        assert eo.max() <= TOL and eS.max() <= TOL, (path, eo, eS)
+        # a zero query reads out exactly zero
+        assert np.all(o[4::H] == 0.0)
+        st.close()

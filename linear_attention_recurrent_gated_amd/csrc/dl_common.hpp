@@ -131,17 +131,6 @@ __device__ __forceinline__ float sum8(float x) {
     return x;
 }
 
-// Sum over all 64 lanes, returned as a wave-uniform value: the 8-lane
-// butterfly, a 16-lane mirror, then row_bcast15 / row_bcast31 (rows 1 and 3
-// add row 0 and 2; rows 2 and 3 add row 1) leave the total in lane 63.
-__device__ __forceinline__ float wave_sum(float x) {
-    x = sum8(x);
-    x += dpp_mov<0x140>(x);   // row_mirror
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
-}
-
 // ---------------------------------------------------------------------------
 // LDS carve-up for staged log entries (step, readout and merge kernels).
 // k entries in the input dtype, decays already exponentiated (alpha), betas.
@@ -329,15 +318,6 @@ __device__ __forceinline__ float xor16_sum(float x) {
 __device__ __forceinline__ float xor32_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Sum over the lanes l, l ^ G, l ^ 2G, ... (G = 8 or 16): the lanes that
-// share a channel group in the chunk layout.
-template <int G>
-__device__ __forceinline__ float cross_sum(float x) {
-    if constexpr (G == 8)
-        x += dpp_mov<0x128>(x);   // row_ror:8
-    return xor32_sum(xor16_sum(x));
 }
 
 // Sum over the lanes that share l % M (M = 2 or 4): rotations inside each

@@ -104,8 +104,9 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The five decode workloads (shapes and distributions are the ones the
-# benchmark plan states; see the recipe in the module docstring).
+# The decode workloads: a tiny single-head case, four serving shapes (GDN,
+# a per-key-decay sweep over L, a ragged multi-layer GDN set and RWKV6) and
+# the gated form; the distributions are in the module docstring.
 TINY_GDN = Workload("tiny-gdn-d64", 1, GDN, batch=1, layers=1, heads=1, d_k=64, d_v=64,
                     steps=256, log_lens=(8,), dtype="f32", qk_l2norm=True, state_std=0.0,
                     decay_mean=0.0, decay_std=1.0)

@@ -1,6 +1,6 @@
 """GPU parity: eager and DeltaLog paths against the float64 oracle.
 
-Tolerance (stated by the benchmark plan): per (unit, head), over all outputs
+Tolerance: per (unit, head), over all outputs
 and over the final state, max |gpu - ref| <= 2e-4 * max(1, max |ref|).
 Sizes here span several workgroups, ragged log tails (steps not a multiple
 of L) and ragged per-sequence log offsets; full-size cases are in

@@ -186,3 +186,10 @@ def test_binding_rejects_bad_tensors():
         st._slots(torch.zeros(3, dtype=torch.int64), 3)
     with pytest.raises(ValueError):
         st._slots(torch.zeros(4, dtype=torch.int32), 3)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No library, no fallback: the binding raises instead of computing anything."""
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        B.load(str(tmp_path / "libdeltalog.so"))

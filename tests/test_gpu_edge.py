@@ -128,19 +128,22 @@ def test_factor_log_payload(wl, L, path):
     run_case(wl, L, (path,), merge_every_step=True, run_oracle=False, on_step=on_step)
 
 
-@pytest.mark.parametrize("form", [B.DL_LOG_WY, B.DL_LOG_FACTORS], ids=["wy", "factors"])
-@pytest.mark.parametrize("wl", [W.GDN_HYBRID.scaled(batch=2, heads=3, steps=20),
-                                W.KDA_SWEEP.scaled(batch=2, heads=3, steps=20),
-                                W.RWKV6_ADD.scaled(batch=2, heads=3, steps=20),
-                                W.GATED.scaled(batch=2, heads=3, steps=20)],
-                         ids=["gdn", "kda", "rwkv6", "gated"])
+_READOUT_CASES = [(w, f) for w in (W.GDN_HYBRID.scaled(batch=2, heads=3, steps=20),
+                                    W.KDA_SWEEP.scaled(batch=2, heads=3, steps=20),
+                                    W.RWKV6_ADD.scaled(batch=2, heads=3, steps=20),
+                                    W.GATED.scaled(batch=2, heads=3, steps=20))
+                  for f in (B.DL_LOG_WY, B.DL_LOG_FACTORS)
+                  if not (w.variant == W.GDN2 and f == B.DL_LOG_WY)]   # gated: factor log only
+
+
+@pytest.mark.parametrize("wl,form", _READOUT_CASES,
+                         ids=[f"{('gdn', 'kda', 'rwkv6', 'gated')[w.variant]}-{'factors' if f else 'wy'}"
+                              for w, f in _READOUT_CASES])
 def test_readout_matches_oracle(wl, form):
     """dl_readout returns S_t q for a fresh q, mid-log and after merges, and changes nothing."""
     L = 6
     H, d = wl.heads, wl.d_k
     P = wl.batch * H
-    if wl.variant == W.GDN2 and form == B.DL_LOG_WY:
-        pytest.skip("the gated form's log is built in the factor form only")
     log(f"case readout {wl.name} form={form}")
     st = B.DecodeState(wl.variant, wl.batch, H, d, L, wl.dtype, log_form=form)
     eg = B.DecodeState(wl.variant, wl.batch, H, d, 0, wl.dtype)

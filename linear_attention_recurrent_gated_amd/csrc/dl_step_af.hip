@@ -203,6 +203,20 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     // ---- loads that need nothing: fill, this wave's rows of S0, the inputs
     const int n = P.fill[pair];
     const int grp = lane >> 3, s = lane & 7;
+    // Head-wise decay: E_n is one scalar, so S0 q and S0 k are formed while
+    // S0 streams in (q and k in S0's column layout, loaded ahead of it) and
+    // scaled by E_n after the barriers.  Only where the registers allow it
+    // (bf16 inputs, logs of up to 16 entries).
+    constexpr bool EARLY_DOT = V == GDN && sizeof(T) == 2 && MV <= 2;
+    float4 qs[SH::NCH], ks[SH::NCH];
+    if constexpr (EARLY_DOT) {
+#pragma unroll
+        for (int m = 0; m < SH::NCH; ++m) {
+            qs[m] = Elem<T>::load4(q + io + col_of(s, m, 0));
+            if constexpr (APPEND)
+                ks[m] = Elem<T>::load4(k + io + col_of(s, m, 0));
+        }
+    }
     const float *Sp = P.base + pair * D * D;
     float4 st[SH::ITER][SH::NCH];
 #pragma unroll
@@ -298,7 +312,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
             for (int i = 0; i < 8; ++i)
                 en[i] = fast_exp(lc[i]);
         }
-        if (ro == 0) {
+        if (!EARLY_DOT && ro == 0) {
             float t[8];
             unpack8<T>(qr.a, qr.b, t);
 #pragma unroll
@@ -321,6 +335,23 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
                     t[i] *= en[i];
                 store8<float>(ske + ch0, t);
             }
+        }
+    }
+    float p0[SH::ITER], x0[SH::ITER];   // S0 q and S0 k per row (head-wise decay)
+    if constexpr (EARLY_DOT) {
+#pragma unroll
+        for (int it = 0; it < SH::ITER; ++it) {
+            float ap = 0.f, ax = 0.f;
+#pragma unroll
+            for (int m = 0; m < SH::NCH; ++m) {
+                ap += st[it][m].x * qs[m].x + st[it][m].y * qs[m].y + st[it][m].z * qs[m].z +
+                      st[it][m].w * qs[m].w;
+                if constexpr (APPEND)
+                    ax += st[it][m].x * ks[m].x + st[it][m].y * ks[m].y + st[it][m].z * ks[m].z +
+                          st[it][m].w * ks[m].w;
+            }
+            p0[it] = ap;
+            x0[it] = ax;
         }
     }
     wait_vm_all();      // this wave's loads and staging have landed
@@ -393,12 +424,15 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     // ---- per row: x = S0 (E k) + sum u_j a_j, a_n = beta (v - x),
     //      o = S0 (E q) + sum r_j a_j + r_n a_n
     float qt[SH::FPL], kt[SH::FPL];
+    if constexpr (!EARLY_DOT) {
 #pragma unroll
-    for (int m = 0; m < SH::NCH; ++m) {
-        f4_to(qt + 4 * m, *reinterpret_cast<const float4 *>(sqe + col_of(s, m, 0)));
-        if constexpr (APPEND)
-            f4_to(kt + 4 * m, *reinterpret_cast<const float4 *>(ske + col_of(s, m, 0)));
+        for (int m = 0; m < SH::NCH; ++m) {
+            f4_to(qt + 4 * m, *reinterpret_cast<const float4 *>(sqe + col_of(s, m, 0)));
+            if constexpr (APPEND)
+                f4_to(kt + 4 * m, *reinterpret_cast<const float4 *>(ske + col_of(s, m, 0)));
+        }
     }
+    const float e_n = EARLY_DOT ? fast_exp(ss[0]) : 0.f;
     float cr[MV], cu[MV];
 #pragma unroll
     for (int mm = 0; mm < MV; ++mm) {
@@ -415,13 +449,18 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     for (int it = 0; it < SH::ITER; ++it) {
         const int row = wave * SH::RPW + it * 8 + grp;
         float ao = 0.f, ax = 0.f;
+        if constexpr (EARLY_DOT) {
+            ao = e_n * p0[it];
+            ax = e_n * x0[it];
+        } else {
 #pragma unroll
-        for (int m = 0; m < SH::NCH; ++m) {
-            ao += st[it][m].x * qt[4 * m] + st[it][m].y * qt[4 * m + 1] +
-                  st[it][m].z * qt[4 * m + 2] + st[it][m].w * qt[4 * m + 3];
-            if constexpr (APPEND)
-                ax += st[it][m].x * kt[4 * m] + st[it][m].y * kt[4 * m + 1] +
-                      st[it][m].z * kt[4 * m + 2] + st[it][m].w * kt[4 * m + 3];
+            for (int m = 0; m < SH::NCH; ++m) {
+                ao += st[it][m].x * qt[4 * m] + st[it][m].y * qt[4 * m + 1] +
+                      st[it][m].z * qt[4 * m + 2] + st[it][m].w * qt[4 * m + 3];
+                if constexpr (APPEND)
+                    ax += st[it][m].x * kt[4 * m] + st[it][m].y * kt[4 * m + 1] +
+                          st[it][m].z * kt[4 * m + 2] + st[it][m].w * kt[4 * m + 3];
+            }
         }
 #pragma unroll
         for (int mm = 0; mm < MV; ++mm) {

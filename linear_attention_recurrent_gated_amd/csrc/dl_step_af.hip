@@ -358,18 +358,27 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     __syncthreads();    // 1: staged factors, Lam_c, per-entry factors, E q, E k
 
     const bool merging = FUSE && APPEND && n == L - 1;
+    // This lane's first channel, recomputed from the thread index at each use
+    // from here on (an empty asm hides it from common-subexpression
+    // elimination), so that the compiler neither keeps nor spills it.
+    auto chan = [] {
+        int t = threadIdx.x;
+        asm volatile("" : "+v"(t));
+        return 8 * ((t & 63) % G);
+    };
+    const int chl = chan();
     float ekv[8];                        // gated: this lane's channels of e * k
     if constexpr (APPEND && V == GDN2)
-        load8<float>(reinterpret_cast<const float *>(smem + ap.off_ek) + ch0, ekv);
+        load8<float>(reinterpret_cast<const float *>(smem + ap.off_ek) + chl, ekv);
     if (n > 0) {
 #pragma unroll
         for (int p = EARLY; p < NP; ++p)
             if (p < npass)
-                load_key_raw<V, D, T>(P, entry_of(p), ch0, pre[p]);
+                load_key_raw<V, D, T>(P, entry_of(p), chl, pre[p]);
     }
     float lc[8];
     if constexpr (V != GDN)
-        load8<float>(slc + ch0, lc);
+        load8<float>(slc + chl, lc);
 
     // ---- r_j = (k_j D(j, c)) . q and u_j = (k_j D(j, c)) . k for this lane's
     //      entry of each pass (the new entry n is this step's k, D = 1); a
@@ -412,7 +421,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
 #pragma unroll
                 for (int i = 0; i < 8; ++i)
                     kd[i] *= f;
-            store8<float>(skd + j * D + ch0, kd);
+            store8<float>(skd + j * D + chan(), kd);
         }
     };
 #pragma unroll
@@ -492,7 +501,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
         // the merged base and the emptied log keeps no copy of it)
         if (wave == 0 && !merging) {
             if (ro == 0) {
-                uint4 *dst = reinterpret_cast<uint4 *>(static_cast<T *>(P.log_k) + (e0 + n) * D + ch0);
+                uint4 *dst = reinterpret_cast<uint4 *>(static_cast<T *>(P.log_k) + (e0 + n) * D + chan());
                 dst[0] = kr.a;
                 if constexpr (sizeof(T) == 4)
                     dst[1] = kr.b;

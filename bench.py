@@ -137,6 +137,18 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def merging_order(batch: int, merging, spread: bool):
+    """Batch order for a step that merges the units in ``merging`` in place:
+    those units first, or (``spread``) evenly spaced through the batch, the
+    other units in their own order in between."""
+    merging = np.asarray(merging)
+    rest = np.setdiff1d(np.arange(batch), merging)
+    if not spread:
+        return np.concatenate([merging, rest])
+    gap = len(rest) // len(merging)
+    return np.insert(rest, np.arange(len(merging)) * gap, merging)
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -322,12 +334,7 @@ def main(argv=None):
             full_next = np.nonzero(fills + np.isin(np.arange(Bt), act[tau]) == L)[0]
             order = None
             if wl.ragged and tau >= prefix and fused and 0 < len(full_next) < Bt:
-                rest = np.setdiff1d(np.arange(Bt), full_next)
-                if path.startswith("af"):
-                    gap = len(rest) // len(full_next)
-                    order = np.insert(rest, np.arange(len(full_next)) * gap, full_next)
-                else:
-                    order = np.concatenate([full_next, rest])
+                order = merging_order(Bt, full_next, spread=path.startswith("af"))
                 order_t = torch.from_numpy(order.astype(np.int64)).to(dev)
                 slot_o = torch.from_numpy(order.astype(np.int32)).to(dev)
             merge_slots = None

@@ -2,6 +2,7 @@
 the one-GPU guard.  No GPU is touched."""
 import os
 
+import numpy as np
 import pytest
 
 import bench
@@ -73,3 +74,30 @@ def test_log_step_bytes_grow_with_fill(cfg):
         fm = bench.form_model(m, path)
         b = [bench.log_step_bytes(fm, c) for c in range(8)]
         assert all(x < y for x, y in zip(b, b[1:]))
+
+
+@pytest.mark.parametrize("spread", [False, True])
+@pytest.mark.parametrize("n", [1, 3, 8, 17, 255])
+def test_merging_order_is_a_permutation(n, spread):
+    rng = np.random.default_rng(n)
+    merging = np.sort(rng.choice(256, n, replace=False))
+    order = bench.merging_order(256, merging, spread)
+    assert sorted(order.tolist()) == list(range(256))
+    pos = np.array([int(np.nonzero(order == u)[0][0]) for u in merging])
+    rest = order[~np.isin(order, merging)]
+    assert np.all(np.diff(rest) > 0)                        # the others keep their order
+    if not spread:
+        assert np.array_equal(np.sort(pos), np.arange(n))   # merging units first
+    else:
+        gap = (256 - n) // n
+        assert np.array_equal(pos, np.arange(n) * (gap + 1))  # evenly spaced
+
+
+def test_suggested_log_lens_of_the_workloads():
+    """The log lengths the traffic model picks for the bench shapes."""
+    from linear_attention_recurrent_gated_amd import binding as B
+    cases = [((B.DL_GDN, 128, B.DL_LOG_FACTORS, 1), 13), ((B.DL_KDA, 128, B.DL_LOG_FACTORS, 1), 10),
+             ((B.DL_RWKV6, 64, B.DL_LOG_WY, 1), 8), ((B.DL_RWKV6, 64, B.DL_LOG_WY, 0), 11)]
+    for (variant, d, form, fuse), L in cases:
+        got, _ = B.dl_suggest_log_len(B.DlDesc(variant, 1, 1, d, d, 0, B.DL_BF16, fuse, form))
+        assert got == L, (variant, form, fuse, got)

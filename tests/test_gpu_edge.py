@@ -300,13 +300,16 @@ def _degenerate_inputs(variant, U, H, d, T, seed=11):
     return q, k, v, g, beta
 
 
+@pytest.mark.parametrize("d,dtype", [(64, "f32"), (128, "bf16")], ids=["d64-f32", "d128-bf16"])
 @pytest.mark.parametrize("variant", [W.GDN, W.KDA, W.RWKV6, W.GDN2], ids=["gdn", "kda", "rwkv6", "gated"])
-def test_degenerate_inputs_parity(variant):
+def test_degenerate_inputs_parity(variant, d, dtype):
     """No write, no decay, zero keys, near-total forgetting and zero queries
     reach the oracle's result on every path (log tail left unmerged until the
     final flush)."""
-    U, H, d, T, L = 2, 6, 64, 21, 8
+    U, H, T, L = 2, 6, 21, 8
     q, k, v, g, beta = _degenerate_inputs(variant, U, H, d, T)
+    # what the kernels read (input dtype) and the same values exactly, for the oracle
+    (q_in, q), (k_in, k), (v_in, v) = (W.store(x, dtype) for x in (q, k, v))
     S0 = (0.3 * np.random.default_rng(3).standard_normal((U, H, d, d))).astype(np.float32)
     P = U * H
     o_ref, S_ref = oracle.run(variant, q.reshape(T, P, d), k.reshape(T, P, d), v.reshape(T, P, d),
@@ -316,14 +319,15 @@ def test_degenerate_inputs_parity(variant):
     paths = ("eager", "af", "af-fused") if variant == W.GDN2 else \
         ("eager", "log", "log-fused", "af", "af-fused")
     for path in paths:
-        st = B.DecodeState(variant, U, H, d, 0 if path == "eager" else L, "f32",
+        st = B.DecodeState(variant, U, H, d, 0 if path == "eager" else L, dtype,
                            merge_on_step=path.endswith("-fused"),
                            log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY)
         st.base.copy_(torch.from_numpy(S0))
         outs = []
         for t in range(T):
-            args = tuple(None if x is None else torch.from_numpy(np.ascontiguousarray(x[t])).cuda()
-                         for x in (q, k, v, g, beta))
+            args = tuple(to_torch(x[t], dtype) for x in (q_in, k_in, v_in)) + \
+                tuple(None if x is None else torch.from_numpy(np.ascontiguousarray(x[t])).cuda()
+                      for x in (g, beta))
             if path == "eager":
                 outs.append(st.step_eager(*args))
             else:

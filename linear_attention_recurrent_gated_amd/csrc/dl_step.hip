@@ -642,13 +642,22 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
             const int mend = APPEND ? n : ct;     // stored columns m < mend
             for (int m0 = 0; m0 < mend; m0 += 8) {
                 float rv[8], uv[8], Rv[8];
+                // sr and su hold entries < ct only: the batch's tail past mend is
+                // whatever the LDS held before, so it is selected away, not
+                // multiplied by zero (a stale Inf or NaN would survive that)
 #pragma unroll
                 for (int t = 0; t < 8; t += 4) {
                     const float4 a = *reinterpret_cast<const float4 *>(sr + m0 + t);
-                    rv[t] = a.x, rv[t + 1] = a.y, rv[t + 2] = a.z, rv[t + 3] = a.w;
+                    const float ra[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        rv[t + e] = (m0 + t + e < mend) ? ra[e] : 0.f;
                     if constexpr (APPEND) {
                         const float4 b = *reinterpret_cast<const float4 *>(su + m0 + t);
-                        uv[t] = b.x, uv[t + 1] = b.y, uv[t + 2] = b.z, uv[t + 3] = b.w;
+                        const float ub[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            uv[t + e] = (m0 + t + e < mend) ? ub[e] : 0.f;
                     }
                 }
 #pragma unroll

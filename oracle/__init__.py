@@ -14,10 +14,12 @@ falls back to it.
 * :mod:`oracle.exact` -- exact rational (``fractions.Fraction``) models used
   to pin the float64 oracle and the deferred base + log algebra.
 
-Parity status: every function here is pinned by the CPU tests
-(``tests/test_oracle_pins.py``): brute-force product expansion, the
-delta-rule write invariant, the identity case, closed forms and the exact
-equality of eager and deferred schedules.  The pages print no worked numeric
+Parity status: every function here is pinned by the CPU tests:
+:func:`run` and :func:`additive_factor` in ``tests/test_oracle_pins.py``
+(brute-force product expansion, the delta-rule write invariant, the identity
+case, closed forms and the exact equality of eager and deferred schedules),
+:func:`readout` in ``tests/test_oracle_readout.py`` (the recurrence's own last
+output and a hand-worked example, with planted mistakes that must fail).  The pages print no worked numeric
 example, so no stored value comes from them.
 """
 from __future__ import annotations

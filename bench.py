@@ -12,15 +12,29 @@ line is printed:
 
   value          the fastest DeltaLog path's state updates/s (one update =
                  one state, one token); its name is in "path"
-  roofline       that path's step kernel: algorithmic bytes per launch over
-                 its average HIP-event duration, against 8 TB/s, and the
-                 counter-measured bytes per launch ("traffic") when the
-                 committed profile matches the sources
+  roofline       that path's step kernel: the method's algorithmic bytes per
+                 update (the measurement plan's byte model) times the updates
+                 one launch processes, over the launch's average HIP-event
+                 duration, against 8 TB/s; the path's own byte model beside
+                 it; the counter-measured bytes per launch ("traffic") when
+                 the committed profile matches the sources
+  write_traffic_reduction
+                 dense-state write bytes of eager over DeltaLog (model, and
+                 from the committed counters when they match the sources)
   eager          the same for the eager path
   other_paths    the same for the other DeltaLog paths
   merge          the separate merge kernels' bytes and fp32 rate
   cpu_baseline   the float64 oracle on the host cores, on a bounded sample
   parity         the sampled GPU outputs and final states against the oracle
+
+The default workload is the ragged 8-layer GDN decode (batch 256, 32 heads,
+d = 128, 4 GiB of fp32 state, L = 32): the largest configuration, and one
+whose working set does not fit the 256 MiB Infinity Cache, so its rates are
+HBM rates.  Its logs fill at staggered steps, so every step merges about
+1/L of the sequences and any window of steps is stationary.  For the other
+workloads every log fills at the same step; the warmup is rounded up to
+whole log periods so that the timed window starts at a period boundary, and
+the JSON line states how many merge steps the window holds.
 
 Usage: python bench.py [--config 1..6] [--L n] [--steps K] [--warmup W] [--paths ...]
 """
@@ -95,6 +109,30 @@ def merge_bytes(m, n):
     return 2 * m["St"] + n * m["E"] + 8
 
 
+def update_bytes(m, L, kind):
+    """The method's algorithmic bytes per state update, whatever the log form
+    (the measurement plan's byte model, with the compact-WY entry size E):
+    eager ``2 St + In + Out``; a DeltaLog step ``St + (L-1)/2 E + E + In +
+    Out`` (the base read, the logged entries read back on average, the
+    append); a whole DeltaLog period adds the amortised merge ``(2 St + L E)
+    / L``.  kind: "eager", "step" or "period"."""
+    St, E, In, Out = m["St"], m["E"], m["In"], m["Out"]
+    if kind == "eager":
+        return 2 * St + In + Out
+    step = St + (L - 1) / 2 * E + E + In + Out
+    if kind == "step":
+        return step
+    return step + (2 * St + L * E) / L
+
+
+def write_bytes(m, L, kind):
+    """Algorithmic bytes written per update: eager writes the state and o; a
+    DeltaLog update writes its log entry, o and 1/L of a merged base."""
+    if kind == "eager":
+        return m["St"] + m["Out"]
+    return m["E"] + m["Out"] + m["St"] / L
+
+
 def merge_flops(wl, n, factors=False):
     """The dense contractions per merged state: W = S Kt^T and S += Z Y (WY),
     S += A Kd^T alone for the additive-factor log and the additive variant."""
@@ -111,8 +149,8 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def counter_traffic(kernel: str, workload: str, log_len: int | None = None):
-    """HBM bytes per launch from a committed counter summary, if it matches the
+def counter_field(kernel: str, workload: str, field: str, log_len: int | None = None):
+    """A number from a committed counter summary, if the summary matches the
     sources and, for a log kernel, the log length it was taken at."""
     path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.counters.md")
     if not os.path.exists(path):
@@ -128,9 +166,32 @@ def counter_traffic(kernel: str, workload: str, log_len: int | None = None):
     if log_len is not None and vals.get("log_len") not in (None, str(log_len)):
         return None
     try:
-        return float(vals["traffic_bytes_per_launch"])
+        return float(vals[field])
     except (KeyError, ValueError):
         return None
+
+
+def counter_traffic(kernel: str, workload: str, log_len: int | None = None):
+    """HBM bytes per launch (calibrated FETCH_SIZE + WRITE_SIZE) from a committed
+    counter summary."""
+    return counter_field(kernel, workload, "traffic_bytes_per_launch", log_len)
+
+
+def counter_write_bytes(kernel: str, workload: str, log_len: int | None = None):
+    """Bytes written per launch (calibrated WRITE_SIZE) from a committed counter summary."""
+    kib = counter_field(kernel, workload, "WRITE_SIZE_KiB_avg", log_len)
+    factor = counter_field(kernel, workload, "write_factor", log_len)
+    return None if kib is None or factor is None else kib * 1024 * factor
+
+
+def warmup_steps(wl: W.Workload, L: int, requested: int | None) -> int:
+    """Untimed steps before the timed window: ``requested`` (default 2 L),
+    rounded up to whole log periods when every log fills at the same step, so
+    the window starts at a period boundary."""
+    w = 2 * L if requested is None else requested
+    if L > 0 and not wl.ragged:
+        w = -(-w // L) * L
+    return w
 
 
 def log(msg):
@@ -154,7 +215,7 @@ def parse_args(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None, help="timed steps (default: the workload's)")
     ap.add_argument("--warmup", type=int, default=None, help="untimed steps before timing")
-    ap.add_argument("--config", type=int, default=2, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--config", type=int, default=4, choices=sorted(W.WORKLOADS))
     ap.add_argument("--L", type=int, default=None, help="log slots (default: the workload's)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--reps", type=int, default=3,
@@ -225,7 +286,7 @@ def main(argv=None):
     wl = W.WORKLOADS[args.config]
     L = args.L or (16 if args.config == 3 else wl.log_lens[0])
     K = args.steps or wl.steps
-    Wu = args.warmup if args.warmup is not None else 2 * L
+    Wu = warmup_steps(wl, L, args.warmup)
     prefix = wl.prefix_steps(L)
     T = prefix + Wu + K
     H, d, Bt, layers = wl.heads, wl.d_k, wl.batch, wl.layers
@@ -254,6 +315,7 @@ def main(argv=None):
     Bb = torch.empty(bshape, dtype=torch.float32, device=dev) if wl.has_beta else None
     # oracle sample: calibrate its speed, then pick how many states it takes
     sample_cap = P
+    cpu_threads = oracle.default_threads()
     if not args.no_cpu_baseline:
         rng = np.random.default_rng(1)
         n_cal = 4
@@ -263,8 +325,7 @@ def main(argv=None):
         tc = time.time()
         oracle.run(wl.variant, qc, qc, qc, gc, bc, threads=1)
         per_core = 16 * n_cal / max(time.time() - tc, 1e-6)
-        threads = min(16, oracle.default_threads())
-        sample_cap = int(max(1, min(P, args.cpu_seconds * per_core * threads / T)))
+        sample_cap = int(max(1, min(P, args.cpu_seconds * per_core * cpu_threads / T)))
     sample = np.unique(np.linspace(0, P - 1, num=sample_cap).round().astype(np.int64))
     sq, sk, sv, sg, sb = [], [], [], [], []
     blocks = [list(range(i, min(T, i + 32))) for i in range(0, T, 32)]
@@ -300,6 +361,19 @@ def main(argv=None):
         if 0 < len(a) < Bt:
             gathers[tau] = (torch.from_numpy(a.astype(np.int64)).to(dev),
                             torch.from_numpy(a.astype(np.int32)).to(dev), len(a))
+    t_first = prefix + Wu
+    fills_at_start = np.zeros(Bt, dtype=np.int64)
+    for tau in range(t_first):
+        fills_at_start[act[tau]] += 1
+        fills_at_start[fills_at_start == L] = 0
+    # steps of the timed window at which some log fills (and merges)
+    f = fills_at_start.copy()
+    merge_steps, merged_units = 0, 0
+    for tau in range(t_first, T):
+        f += 1
+        merge_steps += int((f == L).any())
+        merged_units += int((f == L).sum())
+        f[f == L] = 0
 
     results = {}
     for path in paths:
@@ -316,67 +390,59 @@ def main(argv=None):
         O = torch.zeros((T, U, H, d), dtype=torch.float32, device=dev)
         stream = torch.cuda.current_stream().cuda_stream
         lib = B.load()
-        step_fn = lib.dl_decode_step_eager if path == "eager" else lib.dl_decode_step_log
+        step_fn = lib.dl_decode_step_eager_ordered if path == "eager" else lib.dl_decode_step_log_ordered
         fills = np.zeros(Bt, dtype=np.int64)     # host model of each sequence's log fill
-        keep = []                                # device buffers the plan points into
+        keep = []                                # device index arrays the plan points into
         prefix_out = []                          # gathered inputs / outputs of ragged prefix steps
 
         # every launch of the run, with its arguments, decided before anything runs
         plan = []                                # (tau, kind, handle, args)
-        scatter = []                             # (o, l, tau, row order) of reordered steps
         for tau in range(T):
             # the serving loop knows which logs fill at this step (the host model
             # of the schedule): with ragged logs it merges only those units, and
-            # when the step merges in place it orders the batch so their longer
-            # workgroups do not trail the launch: first for the WY log (its
-            # merge is the long one), spread evenly through the batch for the
-            # factor log (measured: both beat the plain batch order)
+            # when the step merges in place it hands the kernel a row order in
+            # which their longer workgroups do not trail the launch: first for
+            # the WY log (its merge is the long one), spread evenly through the
+            # batch for the factor log; inputs and outputs stay in batch order
             full_next = np.nonzero(fills + np.isin(np.arange(Bt), act[tau]) == L)[0]
-            order = None
+            order_p = None
             if wl.ragged and tau >= prefix and fused and 0 < len(full_next) < Bt:
                 order = merging_order(Bt, full_next, spread=path.startswith("af"))
-                order_t = torch.from_numpy(order.astype(np.int64)).to(dev)
-                slot_o = torch.from_numpy(order.astype(np.int32)).to(dev)
+                order_t = torch.from_numpy(order.astype(np.int32)).to(dev)
+                keep.append(order_t)
+                order_p = order_t.data_ptr()
             merge_slots = None
             if wl.ragged and separate and len(full_next):
                 merge_slots = torch.from_numpy(full_next.astype(np.int32)).to(dev)
+                keep.append(merge_slots)
             for l in range(layers):
                 st = states[l]
                 lo, hi = l * Bt, (l + 1) * Bt
                 if len(act[tau]) == 0:
                     continue
-                if order is not None:
-                    xs = [x[tau, lo:hi].index_select(0, order_t).contiguous() for x in (Q, Kt, V, G)]
-                    xs.append(Bb[tau, lo:hi].index_select(0, order_t).contiguous() if Bb is not None else None)
-                    o = torch.empty((Bt, H, d), dtype=torch.float32, device=dev)
-                    keep.append((xs, slot_o))
-                    scatter.append((o, l, tau, order_t))
-                    rows, sp = Bt, slot_o.data_ptr()
-                elif tau in gathers:
+                if tau in gathers:
                     idx, slot, rows = gathers[tau]
                     xs = [x[tau, lo:hi].index_select(0, idx).contiguous() for x in (Q, Kt, V, G)]
                     xs.append(Bb[tau, lo:hi].index_select(0, idx).contiguous() if Bb is not None else None)
                     o = torch.empty((rows, H, d), dtype=torch.float32, device=dev)
                     prefix_out.append((xs, o, l, tau))
-                    sp = slot.data_ptr()
+                    sp, op = slot.data_ptr(), None
                 else:
                     xs = [Q[tau, lo:hi], Kt[tau, lo:hi], V[tau, lo:hi], G[tau, lo:hi],
                           None if Bb is None else Bb[tau, lo:hi]]
-                    rows, sp, o = Bt, None, O[tau, lo:hi]
+                    rows, sp, op, o = Bt, None, order_p, O[tau, lo:hi]
                 ptrs = [None if x is None else x.data_ptr() for x in xs]
-                plan.append((tau, "step", st.handle, (rows, sp, *ptrs, o.data_ptr(), stream)))
+                plan.append((tau, "step", st.handle, (rows, sp, op, *ptrs, o.data_ptr(), stream)))
                 if path != "eager":
                     if l == 0:
                         fills[act[tau]] += 1
                     if separate and merge_slots is not None:
-                        keep.append(merge_slots)
                         plan.append((tau, "merge", st.handle,
                                      (len(full_next), merge_slots.data_ptr(), B.DL_MERGE_FULL, stream)))
                     elif separate and np.any(fills == L):
                         plan.append((tau, "merge", st.handle, (Bt, None, B.DL_MERGE_FULL, stream)))
                     if l == layers - 1:
                         fills[fills == L] = 0
-        t_first = prefix + Wu
         timed = [(kind, h, a) for tau, kind, h, a in plan if tau >= t_first]
         ev = HipEvents()
         evs = [ev.pair() for _ in timed]
@@ -392,10 +458,6 @@ def main(argv=None):
         run([(kind, h, a) for tau, kind, h, a in plan if tau < t_first])
         for xs, o, l, tau in prefix_out:
             O[tau, l * Bt:(l + 1) * Bt].index_copy_(0, gathers[tau][0], o)
-        fills_at_start = np.zeros(Bt, dtype=np.int64)
-        for tau in range(t_first):
-            fills_at_start[act[tau]] += 1
-            fills_at_start[fills_at_start == L] = 0
         # pass 1 (the measurement): the K steps back to back, HIP events around the
         # region, repeated from the same state; the median repetition is the rate
         snapshot = [st.buf.clone() for st in states]
@@ -429,7 +491,7 @@ def main(argv=None):
                 B.dl_merge(st.handle, Bt, None, B.DL_MERGE_ALL, stream)
         flags = [st.check() for st in states]
         assert not any(flags), f"device flags {flags}"
-        # algorithmic bytes of the timed launches
+        # algorithmic bytes of the timed launches: the path's own byte model
         if path == "eager":
             step_bytes = [eager_bytes(m) * Bt * H] * len(step_ms)
             mbytes, mflops = 0, 0
@@ -453,6 +515,11 @@ def main(argv=None):
                             mflops += layers * H * merge_flops(wl, L, path == "af") * full.sum()
                         f[full] = 0
         kern_s = sum(step_ms) / 1e3
+        # the method's bytes (one figure for every log form): eager, or a DeltaLog
+        # step with (in-step merge) or without (separate merge launch) its share
+        # of the merge
+        kind = "eager" if path == "eager" else ("period" if fused else "step")
+        ub = update_bytes(m0, L, kind)
         res = dict(
             total_ms=total_ms,
             ms_per_step=total_ms / K,
@@ -461,6 +528,10 @@ def main(argv=None):
             updates_per_s=P * K / (total_ms / 1e3),
             step_kernel_avg_us=1e3 * float(np.mean(step_ms)),
             step_kernel_launches=len(step_ms),
+            updates_per_launch=Bt * H,
+            method_bytes_per_update=ub,
+            method_bytes_per_launch=ub * Bt * H,
+            method_GBps=ub * Bt * H / (float(np.mean(step_ms)) / 1e3) / 1e9,
             step_kernel_GBps=sum(step_bytes) / kern_s / 1e9,
             step_bytes_per_launch=float(np.mean(step_bytes)),
             merge_launches=len(merge_ms),
@@ -468,8 +539,6 @@ def main(argv=None):
             merge_bytes=mbytes,
             merge_flops=mflops,
         )
-        for o, l, tau, order_t in scatter:       # back to batch order
-            O[tau, l * Bt:(l + 1) * Bt].index_copy_(0, order_t, o)
         # sampled outputs and final states for the parity check
         su, sh = torch.from_numpy(sample // H).to(dev), torch.from_numpy(sample % H).to(dev)
         res["o_sample"] = O[:, su, sh].double().cpu().numpy()            # [T, n, d]
@@ -482,8 +551,8 @@ def main(argv=None):
         log(f"[bench] {path}: {res['ms_per_step'] * 1e3:.1f} us/step "
             f"[{res['ms_per_step_min'] * 1e3:.1f}, {res['ms_per_step_max'] * 1e3:.1f}], "
             f"{res['updates_per_s']:.3e} upd/s, step kernel {res['step_kernel_avg_us']:.1f} us "
-            f"({res['step_kernel_GBps']:.0f} GB/s), merges {len(merge_ms)} "
-            f"({res['merge_ms_total']:.3f} ms)")
+            f"({res['method_GBps']:.0f} GB/s method bytes, {res['step_kernel_GBps']:.0f} GB/s "
+            f"path bytes), merges {len(merge_ms)} ({res['merge_ms_total']:.3f} ms)")
 
     if args.copy_probe:
         n = args.copy_probe * 2**20 // 4
@@ -501,6 +570,13 @@ def main(argv=None):
                      "batch": Bt, "layers": layers, "heads": H, "d_k": d, "d_v": wl.d_v,
                      "log_len": L, "input_dtype": wl.dtype, "state_dtype": "fp32",
                      "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix}
+    if args.warmup is not None and Wu != args.warmup:
+        out["warmup_requested"] = args.warmup
+    # merges inside the timed window: steps at which some log fills, and the
+    # share of the window's state updates that close a log period (1/L when the
+    # window holds whole periods or the fills are staggered)
+    out["window"] = {"merge_steps": merge_steps, "merged_share": merged_units / (Bt * K),
+                     "whole_periods": bool(wl.ragged or K % L == 0)}
     # the DeltaLog figure is the fastest of the log forms and merge schedules
     # measured here (all are reported): the compact-WY log or the
     # additive-factor log, each with the merge launched after the step that
@@ -516,21 +592,26 @@ def main(argv=None):
     out["ms_per_step_range"] = [r["ms_per_step_min"], r["ms_per_step_max"]]
     out["path"] = main_path
     kname = knames.get(main_path, "eager_step_kernel")
-    out["roofline"] = {"bound": "hbm", "kernel": kname,
-                       "achieved": r["step_kernel_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                       "frac": r["step_kernel_GBps"] / HBM_PEAK_GBPS,
-                       "avg_launch_us": r["step_kernel_avg_us"],
-                       "algorithmic_bytes_per_launch": r["step_bytes_per_launch"],
-                       "traffic": counter_traffic(kname, wl.name, L)}
+
+    def roof(res, kn, log_len):
+        return {"bound": "hbm", "kernel": kn,
+                "achieved": res["method_GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": res["method_GBps"] / HBM_PEAK_GBPS,
+                "traffic": counter_traffic(kn, wl.name, log_len),
+                "avg_launch_us": res["step_kernel_avg_us"],
+                "bytes_per_update": res["method_bytes_per_update"],
+                "updates_per_launch": res["updates_per_launch"],
+                "algorithmic_bytes_per_launch": res["method_bytes_per_launch"],
+                "path_model": {"bytes_per_launch": res["step_bytes_per_launch"],
+                               "achieved": res["step_kernel_GBps"],
+                               "frac": res["step_kernel_GBps"] / HBM_PEAK_GBPS}}
+
+    out["roofline"] = roof(r, kname, L if main_path in knames else None)
     if "eager" in results and main_path != "eager":
         e = results["eager"]
         out["eager"] = {"value": e["updates_per_s"], "ms_per_step": e["ms_per_step"],
                         "ms_per_step_range": [e["ms_per_step_min"], e["ms_per_step_max"]],
-                        "kernel": "eager_step_kernel", "achieved_GBps": e["step_kernel_GBps"],
-                        "frac": e["step_kernel_GBps"] / HBM_PEAK_GBPS,
-                        "avg_launch_us": e["step_kernel_avg_us"],
-                        "algorithmic_bytes_per_launch": e["step_bytes_per_launch"],
-                        "traffic": counter_traffic("eager_step_kernel", wl.name)}
+                        "roofline": roof(e, "eager_step_kernel", None)}
         out["speedup_vs_eager"] = r["updates_per_s"] / e["updates_per_s"]
         # measurably faster: the slowest DeltaLog repetition beats the fastest eager one
         out["faster_in_every_rep"] = bool(r["ms_per_step_max"] < e["ms_per_step_min"])
@@ -539,14 +620,9 @@ def main(argv=None):
         if other == main_path:
             continue
         u = results[other]
-        kn = knames[other]
         others.append({"path": other, "value": u["updates_per_s"], "ms_per_step": u["ms_per_step"],
                        "ms_per_step_range": [u["ms_per_step_min"], u["ms_per_step_max"]],
-                       "kernel": kn, "achieved_GBps": u["step_kernel_GBps"],
-                       "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS,
-                       "avg_launch_us": u["step_kernel_avg_us"],
-                       "algorithmic_bytes_per_launch": u["step_bytes_per_launch"],
-                       "traffic": counter_traffic(kn, wl.name, L)})
+                       "roofline": roof(u, knames[other], L)})
     if others:
         out["other_paths"] = others
     merges = {}
@@ -563,6 +639,14 @@ def main(argv=None):
     if merges:
         out["merge"] = merges
     if main_path in knames:
+        # dense-state write traffic, eager over DeltaLog: the byte model, and the
+        # counters (bytes written per launch) when both summaries match the sources
+        wr = {"model": write_bytes(m0, L, "eager") / write_bytes(m0, L, "log")}
+        we = counter_write_bytes("eager_step_kernel", wl.name)
+        wd = counter_write_bytes(kname, wl.name, L) if main_path.endswith("-fused") else None
+        wr["counters"] = we / wd if we and wd else None
+        wr["counters_path"] = main_path
+        out["write_traffic_reduction"] = wr
         # the log length the traffic model suggests for this shape, form and schedule
         sdesc = B.DlDesc(wl.variant, 1, 1, wl.d_k, wl.d_v, 0,
                          B.DL_BF16 if wl.dtype == "bf16" else B.DL_F32,
@@ -573,15 +657,15 @@ def main(argv=None):
 
     # ---- the oracle on the host cores, same inputs, sampled states
     if not args.no_cpu_baseline:
-        threads = min(16, oracle.default_threads())
         t_start = np.tile(first, layers)[sample // H]
         tc = time.time()
         o_ref, S_ref = oracle.run(wl.variant, np.stack(sq), np.stack(sk), np.stack(sv),
                                   np.stack(sg), np.stack(sb) if sb else None,
-                                  S0.reshape(P, d, d)[sample], t_start, threads=threads)
+                                  S0.reshape(P, d, d)[sample], t_start, threads=cpu_threads)
         dt = time.time() - tc
         n_upd = int(np.sum(T - t_start))
-        out["cpu_baseline"] = {"value": n_upd / dt, "unit": "state updates/s", "cores": threads,
+        out["cpu_baseline"] = {"value": n_upd / dt, "unit": "state updates/s", "cores": cpu_threads,
+                               "affinity_cores": oracle.affinity_cores(),
                                "kind": "oracle", "seconds": dt,
                                "sample": f"{len(sample)} of {P} states (evenly spaced), all {T} steps "
                                          f"({n_upd} updates), float64"}

@@ -150,22 +150,41 @@ typedef struct {
 
 typedef struct dl_state dl_state;   /* opaque host handle */
 
-/* Bytes of device memory a state block of this shape needs (0 if the
- * descriptor is invalid or unsupported). */
+/* State block (the DeltaLog page, Technical Summary, Core Mechanism: Base +
+ * Log -- the live state of each head is a dense base plus a bounded log of
+ * compact updates with their log-decay metadata, with a per-log fill count).
+ * One block holds, for every (unit, head), the fp32 base, the L log slots
+ * and the fill counter, laid out as dl_state_ptrs describes.
+ *
+ * Bytes of device memory a state block of this shape needs (0 if the
+ * descriptor is invalid or unsupported; dl_last_error() says why). */
 size_t dl_state_bytes(const dl_desc *desc);
 
-/* Bind a state block to caller memory `dev_mem` (256-byte aligned, at least
- * dl_state_bytes(desc) bytes) and zero all of it on `stream` (base = 0,
- * logs empty, flags clear).  Write an initial base through dl_state_view
- * after this call (on the same stream, or after synchronising).
- * On success *out owns a new handle; free it with dl_state_free. */
+/* Bind a state block (Core Mechanism: Base + Log, as above) to caller
+ * memory `dev_mem` (device memory, 256-byte aligned, at least
+ * dl_state_bytes(desc) bytes; the caller keeps ownership and must keep it
+ * alive until dl_state_free) and zero all of it on `stream` (base = 0, logs
+ * empty, flags clear).  Write an initial base through dl_state_view after
+ * this call (on the same stream, or after synchronising).  On success *out
+ * owns a new host handle; free it with dl_state_free.  Errors: DL_ERR_INVALID
+ * (NULL or misaligned memory, bad descriptor), DL_ERR_UNSUPPORTED, DL_ERR_SIZE
+ * (bytes too small), DL_ERR_LAUNCH (the zeroing launch failed); *out is then
+ * NULL and nothing was launched except, for DL_ERR_LAUNCH, the failed zeroing. */
 dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void *stream,
                          dl_state **out);
 
-/* Release the handle (not the device memory). NULL is accepted. */
+/* Release the host handle of a state block (Core Mechanism: Base + Log); the
+ * device memory stays the caller's.  NULL is accepted.  Launches already
+ * issued with the handle keep running; the handle itself is no longer
+ * touched by them. */
 dl_status dl_state_free(dl_state *st);
 
-/* Device pointers of the block's parts. */
+/* Device pointers of the block's parts (Core Mechanism: Base + Log: the base,
+ * the log's keys, values or factors, log-decay metadata, betas, key-side
+ * factors and fill counts), written into the caller's dl_state_ptrs struct
+ * (one struct instead of one out-parameter per part).  The pointers stay
+ * valid as long as the caller's memory does.  Errors: DL_ERR_INVALID for a
+ * NULL handle or out. */
 dl_status dl_state_view(const dl_state *st, dl_state_ptrs *out);
 
 /* Eager step (the "eager" decoding the DeltaLog page's Problem section
@@ -200,6 +219,28 @@ dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx
                              const void *q, const void *k, const void *v, const float *g,
                              const float *beta, float *o, void *stream);
 
+/* The two steps above with the order of their workgroups given: workgroups
+ * start in block order, and block b serves input row row_order[b] (all its
+ * heads), so the caller decides which rows start first -- e.g. rows whose log
+ * the step fills and, with merge_on_step, merges in place, whose workgroups
+ * run longer, spread through the launch or placed ahead of the rest -- without
+ * reordering any input or output in memory.  row_order is a device int32
+ * array of `rows` entries, a permutation of 0 .. rows - 1, 4-byte aligned;
+ * NULL gives input order (the plain calls above).  An entry outside
+ * [0, rows) skips its block and raises DL_FLAG_BAD_SLOT; a repeated entry
+ * (then some row is missing) is undefined, as for slot_idx.  Results do not
+ * depend on the order.  This is a scheduling choice for the launches the
+ * DeltaLog page's Kernel Implementation describes (one pass over the
+ * batch's states per step). */
+dl_status dl_decode_step_eager_ordered(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                                       const int32_t *row_order, const void *q, const void *k,
+                                       const void *v, const float *g, const float *beta, float *o,
+                                       void *stream);
+dl_status dl_decode_step_log_ordered(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                                     const int32_t *row_order, const void *q, const void *k,
+                                     const void *v, const float *g, const float *beta, float *o,
+                                     void *stream);
+
 /* Merge (the page's Merge Phase): materialise base + log into the base and
  * empty the log, for the selected rows' units (DL_MERGE_FULL: units whose
  * log holds L entries; DL_MERGE_ALL: every non-empty log).  The update is
@@ -220,8 +261,14 @@ dl_status dl_merge_replay(dl_state *st, int32_t rows, const int32_t *slot_idx, i
                           void *stream);
 
 /* Readout without an update: o = S_logical q for each row's unit, from the
- * base and whatever the log holds (for an eager state, o = S q).
- *   q [rows, H, d_k] in_dtype, o [rows, H, d_v] fp32. */
+ * base and whatever the log holds (for an eager state, o = S q) -- the
+ * readout o = S q of the DeltaLog page's Technical Summary (Problem), taken
+ * here as a query of the current logical state with no token folded in (the
+ * plainest reading of a readout call beside the step calls; the final state
+ * itself is read after dl_merge with DL_MERGE_ALL, through dl_state_view).
+ *   q [rows, H, d_k] in_dtype (16-byte aligned), o [rows, H, d_v] fp32
+ *   (16-byte aligned, must not alias q or the state).  Errors as for the step
+ * calls; a full or empty log is valid here. */
 dl_status dl_readout(dl_state *st, int32_t rows, const int32_t *slot_idx, const void *q,
                      float *o, void *stream);
 

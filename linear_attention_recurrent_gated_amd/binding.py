@@ -55,6 +55,8 @@ _SIGS = {
     "dl_state_view": (_I, [_P, ctypes.POINTER(DlStatePtrs)]),
     "dl_decode_step_eager": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dl_decode_step_log": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "dl_decode_step_eager_ordered": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "dl_decode_step_log_ordered": (_I, [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "dl_merge": (_I, [_P, _I, _P, _I, _P]),
     "dl_merge_replay": (_I, [_P, _I, _P, _I, _P]),
     "dl_readout": (_I, [_P, _I, _P, _P, _P, _P]),
@@ -144,6 +146,18 @@ def dl_decode_step_eager(handle, rows, slot_idx, q, k, v, g, beta, o, stream) ->
 
 def dl_decode_step_log(handle, rows, slot_idx, q, k, v, g, beta, o, stream) -> None:
     _check(load().dl_decode_step_log(handle, rows, slot_idx, q, k, v, g, beta, o, stream))
+
+
+def dl_decode_step_eager_ordered(handle, rows, slot_idx, row_order, q, k, v, g, beta, o,
+                                 stream) -> None:
+    _check(load().dl_decode_step_eager_ordered(handle, rows, slot_idx, row_order, q, k, v, g, beta,
+                                               o, stream))
+
+
+def dl_decode_step_log_ordered(handle, rows, slot_idx, row_order, q, k, v, g, beta, o,
+                               stream) -> None:
+    _check(load().dl_decode_step_log_ordered(handle, rows, slot_idx, row_order, q, k, v, g, beta,
+                                             o, stream))
 
 
 def dl_merge(handle, rows, slot_idx, mode, stream) -> None:
@@ -275,22 +289,31 @@ class DecodeState:
                                     device=self.buf.device)
         return self._tensor("o", o, self.torch.float32, (rows, self.heads, self.d))
 
-    def step_eager(self, q, k, v, g, beta=None, o=None, slot_idx=None, stream=None):
+    def _order(self, row_order, rows):
+        if row_order is None:
+            return None
+        return self._tensor("row_order", row_order, self.torch.int32, (rows,)).data_ptr()
+
+    def step_eager(self, q, k, v, g, beta=None, o=None, slot_idx=None, stream=None,
+                   row_order=None):
         rows, sp = self._rows(q, slot_idx)
         self._check_inputs(rows, q, k, v, g, beta)
         o = self._out(rows, o)
-        dl_decode_step_eager(self.handle, rows, sp, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                             g.data_ptr(), None if beta is None else beta.data_ptr(),
-                             o.data_ptr(), self._stream(stream))
+        dl_decode_step_eager_ordered(self.handle, rows, sp, self._order(row_order, rows),
+                                     q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                     None if beta is None else beta.data_ptr(), o.data_ptr(),
+                                     self._stream(stream))
         return o
 
-    def step_log(self, q, k, v, g, beta=None, o=None, slot_idx=None, stream=None):
+    def step_log(self, q, k, v, g, beta=None, o=None, slot_idx=None, stream=None,
+                 row_order=None):
         rows, sp = self._rows(q, slot_idx)
         self._check_inputs(rows, q, k, v, g, beta)
         o = self._out(rows, o)
-        dl_decode_step_log(self.handle, rows, sp, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                           g.data_ptr(), None if beta is None else beta.data_ptr(),
-                           o.data_ptr(), self._stream(stream))
+        dl_decode_step_log_ordered(self.handle, rows, sp, self._order(row_order, rows),
+                                   q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                   None if beta is None else beta.data_ptr(), o.data_ptr(),
+                                   self._stream(stream))
         return o
 
     def merge(self, mode: int = DL_MERGE_FULL, rows: int | None = None, slot_idx=None,

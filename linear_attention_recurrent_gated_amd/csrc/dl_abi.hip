@@ -167,6 +167,15 @@ dl::Launch launch_of(const dl_state *st, void *stream) {
     return dl::Launch{static_cast<hipStream_t>(stream), st->ev_start, st->ev_stop};
 }
 
+// The block's parameters for one step launch over `rows` rows, taken in
+// `row_order` (NULL: input order).
+dl::Params with_rows(const dl::Params &base, int32_t rows, const int32_t *row_order) {
+    dl::Params p = base;
+    p.rows = rows;
+    p.row_order = row_order;
+    return p;
+}
+
 // Result of one launch; a launch consumes the events dl_time_next_launch armed.
 dl_status launched(dl_state *st, hipError_t e, const char *what) {
     st->ev_start = nullptr;
@@ -219,6 +228,8 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.dtype = desc->in_dtype;
     p.flags = reinterpret_cast<int *>(m + l.off_flags);
     p.fuse = desc->merge_on_step;
+    p.rows = 0;
+    p.row_order = nullptr;
     p.af = factors_form(*desc) ? 1 : 0;
     // Stream the state (nontemporal loads and stores) when what the steps
     // re-read does not fit MI355X's 256 MiB Infinity Cache.  Eager: the state
@@ -271,25 +282,37 @@ dl_status dl_state_view(const dl_state *st, dl_state_ptrs *out) {
     return ok();
 }
 
-dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_idx,
-                               const void *q, const void *k, const void *v, const float *g,
-                               const float *beta, float *o, void *stream) {
+dl_status dl_decode_step_eager_ordered(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                                       const int32_t *row_order, const void *q, const void *k,
+                                       const void *v, const float *g, const float *beta, float *o,
+                                       void *stream) {
     dl_status s = check_step_args(st, rows, slot_idx, q, k, v, g, beta, o);
     if (s != DL_OK)
         return s;
+    if (row_order && !aligned(row_order, 4))
+        return fail(DL_ERR_INVALID, "row_order must be 4-byte aligned");
     if (rows == 0)
         return ok();
-    return launched(st, dl::launch_eager(st->p, rows, slot_idx, q, k, v, g, beta, o,
-                                         launch_of(st, stream)),
+    const dl::Params p = with_rows(st->p, rows, row_order);
+    return launched(st, dl::launch_eager(p, rows, slot_idx, q, k, v, g, beta, o, launch_of(st, stream)),
                     "eager step launch");
 }
 
-dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx,
-                             const void *q, const void *k, const void *v, const float *g,
-                             const float *beta, float *o, void *stream) {
+dl_status dl_decode_step_eager(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                               const void *q, const void *k, const void *v, const float *g,
+                               const float *beta, float *o, void *stream) {
+    return dl_decode_step_eager_ordered(st, rows, slot_idx, nullptr, q, k, v, g, beta, o, stream);
+}
+
+dl_status dl_decode_step_log_ordered(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                                     const int32_t *row_order, const void *q, const void *k,
+                                     const void *v, const float *g, const float *beta, float *o,
+                                     void *stream) {
     dl_status s = check_step_args(st, rows, slot_idx, q, k, v, g, beta, o);
     if (s != DL_OK)
         return s;
+    if (row_order && !aligned(row_order, 4))
+        return fail(DL_ERR_INVALID, "row_order must be 4-byte aligned");
     if (st->desc.log_len < 1)
         return fail(DL_ERR_INVALID, "this state has no log (log_len = 0)");
     s = check_lds(st);
@@ -298,10 +321,17 @@ dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx
     if (rows == 0)
         return ok();
     const dl::Launch ln = launch_of(st, stream);
+    const dl::Params p = with_rows(st->p, rows, row_order);
     return launched(st,
-                    st->p.af ? dl::launch_af_step(st->p, rows, slot_idx, q, k, v, g, beta, o, ln)
-                             : dl::launch_log_step(st->p, rows, slot_idx, q, k, v, g, beta, o, ln),
+                    p.af ? dl::launch_af_step(p, rows, slot_idx, q, k, v, g, beta, o, ln)
+                         : dl::launch_log_step(p, rows, slot_idx, q, k, v, g, beta, o, ln),
                     "log step launch");
+}
+
+dl_status dl_decode_step_log(dl_state *st, int32_t rows, const int32_t *slot_idx,
+                             const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *o, void *stream) {
+    return dl_decode_step_log_ordered(st, rows, slot_idx, nullptr, q, k, v, g, beta, o, stream);
 }
 
 static dl_status merge_common(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,

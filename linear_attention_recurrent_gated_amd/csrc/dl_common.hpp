@@ -36,6 +36,10 @@ struct Params {
     int fuse;          // 1: the log step that fills a log merges it
     int af;            // 1: additive-factor log (delta-rule variants): log_v holds
                        //    the fp32 factors a_j, no betas, no R
+    // per launch: the rows of this call and, optionally, the order the step
+    // workgroups take them in (a device permutation of 0 .. rows - 1)
+    int rows;
+    const int *row_order;
 };
 
 template <int D>
@@ -348,6 +352,21 @@ __device__ __forceinline__ void load_to_lds(const void *src, unsigned char *lds)
 // s_waitcnt vmcnt(0), leaving the other counters free (gfx9 encoding:
 // vmcnt bits 3:0 and 15:14 zero, expcnt 6:4 and lgkmcnt 11:8 at their maxima).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The input row and head a step workgroup serves.  Workgroups are
+// dispatched in block order, so a caller-supplied row_order decides which
+// rows start first (e.g. rows whose log merges in this step, which run
+// longer, ahead of the rest); without one, block b serves row b / heads.
+// Returns -1 for an order entry outside [0, rows).
+__device__ __forceinline__ int step_row(const Params &P, int &h) {
+    const int b = blockIdx.x;
+    const int rb = b / P.heads;
+    h = b - rb * P.heads;
+    if (!P.row_order)
+        return rb;
+    const int r = P.row_order[rb];
+    return (r >= 0 && r < P.rows) ? r : -1;
+}
 
 // Raise a device flag and poison a row's outputs (a rejected row).
 __device__ __forceinline__ void reject_row(const Params &P, float *orow, int D, int flag) {

@@ -54,8 +54,13 @@ eager_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restric
                   const float *__restrict__ beta, float *__restrict__ o) {
     using SH = Shape<D>;
     const int H = P.heads;
-    const int pr = blockIdx.x;                  // input row * H + head
-    const int r = pr / H, h = pr - r * H;
+    int h;
+    const int r = step_row(P, h);
+    if (r < 0) {
+        reject_row(P, nullptr, D, DL_FLAG_BAD_SLOT);
+        return;
+    }
+    const int pr = r * H + h;                   // input row * H + head
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 3, s = lane & 7;
     float *orow = o + (size_t)pr * D;
@@ -450,8 +455,13 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
     constexpr bool DELTA = V != RWKV6;
     extern __shared__ __align__(16) unsigned char smem[];
     const int H = P.heads, L = P.L;
-    const int pr = blockIdx.x;
-    const int r = pr / H, h = pr - r * H;
+    int h;
+    const int r = step_row(P, h);
+    if (r < 0) {
+        reject_row(P, nullptr, D, DL_FLAG_BAD_SLOT);
+        return;
+    }
+    const int pr = r * H + h;                   // input row * H + head
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float *orow = o + (size_t)pr * D;
 

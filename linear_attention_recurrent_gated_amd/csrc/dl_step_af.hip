@@ -176,8 +176,13 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     constexpr int G = KL::G, RP = KL::RP, PASS = 4 * RP;   // entries per pass of the four waves
     extern __shared__ __align__(16) unsigned char smem[];
     const int H = P.heads, L = P.L;
-    const int pr = blockIdx.x;
-    const int r = pr / H, h = pr - r * H;
+    int h;
+    const int r = step_row(P, h);
+    if (r < 0) {
+        reject_row(P, nullptr, D, DL_FLAG_BAD_SLOT);
+        return;
+    }
+    const int pr = r * H + h;                   // input row * H + head
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float *orow = o + (size_t)pr * D;
 

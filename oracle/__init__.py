@@ -55,9 +55,20 @@ def _load(path: str | None = None):
     return _libs[key]
 
 
-def default_threads() -> int:
-    """Every core in this process's affinity mask."""
+def affinity_cores() -> int:
+    """Cores in this process's affinity mask."""
     return len(os.sched_getaffinity(0))
+
+
+def default_threads() -> int:
+    """Every core in this process's affinity mask, capped by ``OMP_NUM_THREADS``
+    when that is set (a host that shares its cores sets it to this process's
+    share)."""
+    n = affinity_cores()
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return n
 
 
 def _f32(a):

@@ -13,6 +13,7 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 import torch
 
+import bench
 import oracle
 from linear_attention_recurrent_gated_amd import binding as B
 from linear_attention_recurrent_gated_amd import workloads as W
@@ -41,7 +42,8 @@ class Case:
 
 def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
              steps: int | None = None, pairs=None, merge_every_step: bool | None = None,
-             run_oracle: bool = True, threads: int | None = None, on_step=None) -> Case:
+             run_oracle: bool = True, threads: int | None = None, on_step=None,
+             bench_schedule: bool = False) -> Case:
     """Run ``paths`` (subset of "eager", "log", "log-replay", "log-fused",
     "af", "af-fused") over the workload.
 
@@ -51,6 +53,10 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
 
     ``pairs``: selected flat pair indices (unit_total * H + head) to record;
     None records all.  ``on_step(tau, states)`` is called after each step.
+    ``bench_schedule``: launch what the benchmark launches for ragged logs --
+    separate merges name only the units whose logs are full (``slot_idx``),
+    and a step that merges in place takes its rows in the benchmark's order
+    (``row_order``) -- instead of a merge over every unit after each step.
     """
     H, d, Bt, layers = wl.heads, wl.d_k, wl.batch, wl.layers
     T = wl.total_steps(L) if steps is None else steps
@@ -60,7 +66,8 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
     first = W.first_active_step(wl, L, seed)                     # [batch]
     first_u = np.tile(first, layers)                             # [units_total]
     if merge_every_step is None:
-        merge_every_step = wl.ragged
+        merge_every_step = wl.ragged and not bench_schedule
+    fills = np.zeros(Bt, dtype=np.int64)                         # host model of the schedule
 
     S0 = W.initial_state(wl, seed)                               # [U, H, d, d]
     states = {}
@@ -108,11 +115,18 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
                 g_sel.append(s.g.reshape(P, -1)[sel] if wl.channel_decay else s.g.reshape(P)[sel])
                 if s.beta is not None:
                     b_sel.append(s.beta.reshape((P,) if wl.beta_width == 1 else (P, -1))[sel])
+            act = np.nonzero(first <= tau)[0]
+            # units whose logs this step fills (the benchmark's host model)
+            full_next = np.nonzero(fills + np.isin(np.arange(Bt), act) == L)[0]
             for path in paths:
                 o_full = torch.zeros((wl.units_total, H, d), dtype=torch.float32, device="cuda")
+                order = None
+                if bench_schedule and path.endswith("-fused") and len(act) == Bt \
+                        and 0 < len(full_next) < Bt:
+                    order = torch.from_numpy(bench.merging_order(
+                        Bt, full_next, spread=path.startswith("af")).astype(np.int32)).cuda()
                 for l in range(layers):
                     st = states[path][l]
-                    act = np.nonzero(first <= tau)[0]
                     lo, hi = l * Bt, (l + 1) * Bt
                     if len(act) == 0:
                         continue
@@ -128,14 +142,20 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
                     if path == "eager":
                         o = st.step_eager(*args, slot_idx=slot)
                     else:
-                        o = st.step_log(*args, slot_idx=slot)
-                        if merge_every_step or (tau + 1) % L == 0:
+                        o = st.step_log(*args, slot_idx=slot, row_order=order)
+                        if bench_schedule and wl.ragged:
+                            if not path.endswith("-fused") and len(full_next):
+                                st.merge(B.DL_MERGE_FULL, slot_idx=torch.from_numpy(
+                                    full_next.astype(np.int32)).cuda(), replay=(path == "log-replay"))
+                        elif merge_every_step or (tau + 1) % L == 0:
                             st.merge(B.DL_MERGE_FULL, replay=(path == "log-replay"))
                     if idx is None:
                         o_full[lo:hi] = o
                     else:
                         o_full[lo:hi].index_copy_(0, idx, o)
                 rec[path].append(o_full[sel_u_t, sel_h_t])
+            fills[act] += 1
+            fills[fills == L] = 0
             if on_step is not None:
                 on_step(tau, states)
         if bi % 8 == 0:

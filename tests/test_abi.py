@@ -112,6 +112,8 @@ def test_null_handle_is_rejected(lib):
     p = ctypes.c_void_p(4096)
     assert lib.dl_decode_step_eager(None, 1, None, p, p, p, p, p, p, None) == B.DL_ERR_INVALID
     assert lib.dl_decode_step_log(None, 1, None, p, p, p, p, p, p, None) == B.DL_ERR_INVALID
+    assert lib.dl_decode_step_eager_ordered(None, 1, None, None, p, p, p, p, p, p, None) == B.DL_ERR_INVALID
+    assert lib.dl_decode_step_log_ordered(None, 1, None, None, p, p, p, p, p, p, None) == B.DL_ERR_INVALID
     assert lib.dl_merge(None, 1, None, 0, None) == B.DL_ERR_INVALID
     assert lib.dl_merge_replay(None, 1, None, 0, None) == B.DL_ERR_INVALID
     assert lib.dl_readout(None, 1, None, p, p, None) == B.DL_ERR_INVALID

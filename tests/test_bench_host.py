@@ -101,3 +101,48 @@ def test_suggested_log_lens_of_the_workloads():
     for (variant, d, form, fuse), L in cases:
         got, _ = B.dl_suggest_log_len(B.DlDesc(variant, 1, 1, d, d, 0, B.DL_BF16, fuse, form))
         assert got == L, (variant, form, fuse, got)
+
+
+# The measurement plan's table of algorithmic bytes per state update (eager,
+# and DeltaLog averaged over a log period with the merge amortised).
+SURVEY_BYTES = [
+    (1, 8, 33_800, 24_372), (2, 16, 132_360, 79_956),
+    (3, 1, 132_868, 200_460), (3, 4, 132_868, 103_698), (3, 8, 132_868, 89_370),
+    (3, 16, 132_868, 85_290), (3, 32, 132_868, 89_418), (3, 64, 132_868, 103_818),
+    (4, 32, 132_360, 80_020), (5, 32, 33_664, 27_264),
+]
+
+
+@pytest.mark.parametrize("cfg,L,eager,period", SURVEY_BYTES)
+def test_update_bytes_match_the_plan_table(cfg, L, eager, period):
+    m = bench.byte_model(W.WORKLOADS[cfg])
+    assert bench.update_bytes(m, L, "eager") == eager
+    assert bench.update_bytes(m, L, "period") == pytest.approx(period, abs=0.5)
+    # the step share leaves out exactly the amortised merge
+    merge = (2 * m["St"] + L * m["E"]) / L
+    assert bench.update_bytes(m, L, "step") == pytest.approx(period - merge)
+
+
+@pytest.mark.parametrize("cfg,L,reduction", [(1, 8, 5.9), (2, 16, 12.9), (4, 32, 21.4), (5, 32, 13.0)])
+def test_write_reduction_model(cfg, L, reduction):
+    m = bench.byte_model(W.WORKLOADS[cfg])
+    r = bench.write_bytes(m, L, "eager") / bench.write_bytes(m, L, "log")
+    assert r == pytest.approx(reduction, abs=0.05)
+
+
+def test_warmup_rounds_to_whole_periods_only_when_logs_fill_together():
+    assert bench.warmup_steps(W.WORKLOADS[2], 16, 5) == 16
+    assert bench.warmup_steps(W.WORKLOADS[2], 16, 32) == 32
+    assert bench.warmup_steps(W.WORKLOADS[2], 16, None) == 32
+    assert bench.warmup_steps(W.WORKLOADS[4], 32, 5) == 5          # ragged: any window
+    assert bench.warmup_steps(W.WORKLOADS[2], 16, 0) == 0
+
+
+def test_default_workload_is_the_largest():
+    args = bench.parse_args([])
+    wl = W.WORKLOADS[args.config]
+    assert wl.name == "gdn-b256-l8-h32-d128-ragged"
+    states = wl.units_total * wl.heads * wl.d_k * wl.d_v * 4
+    assert states == 4 * 2**30 and all(
+        w.units_total * w.heads * w.d_k * w.d_v <= wl.units_total * wl.heads * wl.d_k * wl.d_v
+        for w in W.WORKLOADS.values())

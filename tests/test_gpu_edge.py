@@ -229,6 +229,50 @@ def test_permuted_slots_match_identity(form):
     assert torch.equal(a.base, b.base) and torch.equal(a.fill, b.fill)
 
 
+@pytest.mark.parametrize("path", ["eager", "wy", "wy-fused", "factors", "factors-fused"])
+def test_row_order_changes_nothing(path):
+    """Workgroups taken in a caller-given row order produce bit-identical
+    outputs, states and logs; an order entry out of range is flagged."""
+    wl = W.GDN_LARGE.scaled(batch=7, layers=1, heads=3, steps=11)
+    H, d, L, Bt = wl.heads, wl.d_k, 4, wl.batch
+    form = B.DL_LOG_FACTORS if path.startswith("factors") else B.DL_LOG_WY
+    Lp = 0 if path == "eager" else L
+    fused = path.endswith("-fused")
+    a = B.DecodeState(wl.variant, Bt, H, d, Lp, wl.dtype, log_form=form, merge_on_step=fused)
+    b = B.DecodeState(wl.variant, Bt, H, d, Lp, wl.dtype, log_form=form, merge_on_step=fused)
+    S0 = torch.from_numpy(W.initial_state(wl)).cuda()
+    a.base.copy_(S0)
+    b.base.copy_(S0)
+    rng = np.random.default_rng(3)
+    for tau in range(wl.steps):
+        _, args = _inputs(wl, tau)
+        order = torch.from_numpy(rng.permutation(Bt).astype(np.int32)).cuda()
+        if path == "eager":
+            oa = a.step_eager(*args)
+            ob = b.step_eager(*args, row_order=order)
+        else:
+            oa = a.step_log(*args)
+            ob = b.step_log(*args, row_order=order)
+            if not fused and (tau + 1) % L == 0:
+                a.merge()
+                b.merge()
+        assert torch.equal(oa, ob), f"outputs differ at step {tau}"
+    assert torch.equal(a.buf, b.buf)
+    assert a.check() == 0 and b.check() == 0
+    bad = torch.tensor([0, 1, 2, 3, 4, 5, 9], dtype=torch.int32, device="cuda")
+    _, args = _inputs(wl, wl.steps)
+    fill = b.fill.clone()
+    if path == "eager":
+        o = b.step_eager(*args, row_order=bad)
+    else:
+        o = b.step_log(*args, row_order=bad)
+    assert b.check() == B.DL_FLAG_BAD_SLOT
+    assert not torch.isnan(o[:6]).any()
+    assert path == "eager" or torch.equal(b.fill[6], fill[6])   # row 6 was never served
+    a.close()
+    b.close()
+
+
 def test_zero_rows_and_argument_errors():
     wl = W.GDN_HYBRID.scaled(batch=2, heads=2, steps=1)
     H, d = wl.heads, wl.d_k
@@ -244,6 +288,8 @@ def test_zero_rows_and_argument_errors():
     mis = ctypes.c_void_p(q.data_ptr() + 2)
     assert lib.dl_decode_step_eager(h, 2, None, mis, ptr(k), ptr(v), ptr(g), ptr(beta), ptr(o), None) == B.DL_ERR_INVALID
     assert lib.dl_merge(h, 2, None, 5, None) == B.DL_ERR_INVALID
+    assert lib.dl_decode_step_log_ordered(h, 2, None, mis, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta),
+                                          ptr(o), None) == B.DL_ERR_INVALID   # misaligned order
     e = B.DecodeState(wl.variant, 2, H, d, 0, wl.dtype)
     assert lib.dl_decode_step_log(e.handle, 2, None, ptr(q), ptr(k), ptr(v), ptr(g), ptr(beta), ptr(o), None) == B.DL_ERR_INVALID
     assert st.check() == 0 and int(st.fill.max()) == 0

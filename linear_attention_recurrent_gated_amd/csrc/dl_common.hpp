@@ -115,6 +115,12 @@ struct Elem<uint16_t> {
     }
 };
 
+// Eight bf16 values (one 16-byte word) as floats.
+__device__ __forceinline__ void unpack_bf16x8(const uint4 &u, float *x) {
+    x[0] = bf16_lo(u.x), x[1] = bf16_hi(u.x), x[2] = bf16_lo(u.y), x[3] = bf16_hi(u.y);
+    x[4] = bf16_lo(u.z), x[5] = bf16_hi(u.z), x[6] = bf16_lo(u.w), x[7] = bf16_hi(u.w);
+}
+
 __device__ __forceinline__ void f4_to(float *dst, float4 x) {
     dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
 }

@@ -359,6 +359,29 @@ __device__ __forceinline__ void load_to_lds(const void *src, unsigned char *lds)
 // vmcnt bits 3:0 and 15:14 zero, expcnt 6:4 and lgkmcnt 11:8 at their maxima).
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier for data staged with direct-to-LDS loads while at most N
+// later loads of each wave (e.g. of a tile that is used after the barrier)
+// stay in flight: each wave waits until at most N of its loads are
+// outstanding -- loads complete in issue order, so its staging has landed --
+// and its LDS stores have completed, then all waves meet.  Unlike
+// __syncthreads() this does not wait for the N later loads (a workgroup
+// fence would, since the staging loads write LDS).  The asm's memory clobber
+// keeps the compiler from moving memory accesses across it.
+template <int N>
+__device__ __forceinline__ void barrier_after_staging() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | 0x0070);
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N): wait until at most N of this wave's vector memory
+// loads are outstanding (they complete in issue order), other counters free.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt has 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (((N >> 4) & 3) << 14) | 0x0F70);
+}
+
 // The input row and head a step workgroup serves.  Workgroups are
 // dispatched in block order, so a caller-supplied row_order decides which
 // rows start first (e.g. rows whose log merges in this step, which run

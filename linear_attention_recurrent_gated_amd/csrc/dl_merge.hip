@@ -5,25 +5,14 @@
 //
 // merge_wy_kernel -- the logged transforms folded in WY/UT form, the block
 // form the CARVE page (abstract: WY-form triangular chunk solver) and Gated
-// DeltaNet-2 (chunkwise WY algorithm) use.  For a chunk of C = 16 entries
-// with chunk-local cumulative log-decay Lam_j (per key channel):
-//   Kt_j = k_j exp(Lam_j)                         (decayed keys)
-//   W    = S Kt^T                                 (d_v x C, MFMA)
-//   M_ij = beta_j sum_c k_i k_j exp(Lam_j - Lam_i)   for i < j
-//   Kh_j = k_j exp(Lam_C - Lam_j)
-//   Y    = diag(beta) (I + M)^{-1} Kh             (C x d_k, back substitution)
-//   S'   = S diag(exp(Lam_C)) + (V^T - W) Y       (MFMA)
-// (additive variant: S' = S diag(exp(Lam_C)) + V^T Kh).  This is the
-// recurrence unrolled over the chunk: with u_j = beta_j (v_j - S_{j-1}
-// diag(alpha_j) k_j), S_C = S_0 diag(exp Lam_C) + sum_j u_j Kh_j^T and the
-// u_j solve U (I + M) = (V^T - W) diag(beta).  Chunks run one after the
-// other; decays never exceed 1 inside a chunk, so nothing overflows.
-//
-// The base stays in registers for the whole merge, in the MFMA operand
-// layout of v_mfma_f32_16x16x4_f32 (lane l: row l % 16 of a 16-row value
-// tile, column sub-block l / 16): those registers are the B operand of
-// W^T = Kt S^T and, read as 16 x 16 output tiles, the accumulators of the
-// update S'^T = diag(exp Lam_C) S^T + Y^T Z^T -- no transposes, no reloads.
+// DeltaNet-2 (chunkwise WY algorithm) use.  The log step already keeps the
+// triangular factor of that form, R = (I + N)^{-1}, one column per appended
+// entry, so the merge only contracts: with u_j = beta_j (v_j - S_{j-1}
+// diag(alpha_j) k_j) the recurrence unrolls to S_c = S_0 diag(E_c) + sum_j
+// u_j (k_j D(j, c))^T, and the u_j are the columns of (V^T - S_0 Kt^T) R
+// diag(beta) -- see the kernel below.  With decays of at most 1 (g <= 0) every
+// decay factor is exp of a non-positive difference of the cumulative
+// log-decays, so nothing overflows.
 //
 // merge_replay_kernel -- the same result by replaying the logged steps one
 // by one on the vector ALUs (cross-check).
@@ -123,219 +112,337 @@ __global__ void __launch_bounds__(256) merge_replay_kernel(Params P, const int *
 }
 
 // ---------------------------------------------------------------------------
-// WY merge (MFMA).  Four waves per (unit, head); each holds D/4 value rows of
-// the base in MFMA layout for the whole merge.  Per chunk, the key side
-// (decayed keys, pairwise-decay Gram, Y by back substitution) is built in
-// LDS by all threads in three short phases, then each wave runs the two
-// contractions on its rows.  The value loads of the chunk are issued before
-// the key-side phases so they overlap them.
+// WY merge (MFMA).
+//
+// With n logged entries, E_j = exp(Lam_j), D(j, c) = exp(Lam_c - Lam_j) and
+// the key-side factor R = (I + N)^{-1} that the log step keeps (packed
+// columns, one appended per entry), the merged base is
+//   S' = S0 diag(E_c) + Z Y,   Z = V^T - S0 Kt^T,   Kt_j = E_j k_j,
+//   Y = R Q,                   Q_i = beta_i k_i D(i, c)
+// (additive variant: R = I, beta = 1, Z = V^T) -- the readout formula of the
+// log step written for every query at once, so the merge needs no Gram
+// matrix and no triangular solve: R is read back from the log.  All three
+// products run on v_mfma_f32_16x16x4_f32 in 16-entry chunks:
+//   phase A  z_c = V_c^T - S0 Kt_c^T for every chunk, with the original base;
+//   phase B  S0 <- S0 diag(E_c), then per chunk Y_c = R_c Q (each wave a
+//            share of its column blocks, through LDS) and S0 += z_c Y_c.
+// The base stays in registers in the MFMA operand layout (lane l: row l % 16
+// of a 16-row value tile, column sub-block l / 16): the B operand of W^T =
+// Kt S0^T and, read as 16 x 16 tiles of S0^T, the accumulators of the
+// update -- no transposes, no reloads.
+//
+// A pair's D value rows may be split over NS = D / (16 NW NIT) workgroups
+// (the longest logs, whose chunk tiles do not fit beside a whole base in
+// registers); every workgroup of a pair stages the pair's key side and builds
+// Y for itself (cheap next to the base traffic), and they are dispatched 8
+// blocks apart -- on one XCD, whose L2 then serves the repeated key reads.  The log's keys, decays and R go to LDS
+// with direct-to-LDS loads issued before the base loads, so the key side is
+// ready while the base is still in flight.
+//
+// The fill count is read and reset through tickets in its upper half: each
+// workgroup of a pair adds 1 << 16 and reads the count in the lower half; the
+// one that takes the last ticket writes the count back (0 when the pair
+// merges), so no workgroup of a pair can read a count another one reset.
 // ---------------------------------------------------------------------------
-template <int V, int D, typename T, bool NT>
-__global__ void __launch_bounds__(256, (V == KDA && D == 128) ? 3 : 1)
-merge_wy_kernel(Params P, const int *__restrict__ slot_idx, int mode) {
-    constexpr int C = 16;               // entries per WY chunk
-    constexpr int NIT = D / 64;         // 16-row value tiles per wave
-    constexpr int NM = D / 16;          // 16-column blocks
-    constexpr int KS = D + 4;           // padded LDS row stride (floats)
-    __shared__ __align__(16) float sKt[C * KS];   // k_j exp(Lam_j)
-    __shared__ __align__(16) float sY[C * KS];    // rows of diag(beta)(I+M)^{-1} Kh
-    __shared__ __align__(16) float sK[C * KS];    // keys, fp32
-    __shared__ __align__(16) float sLam[C * KS];  // chunk-local cumulative log-decay
-    __shared__ float sM[C * C];                   // beta_j G_ij, i < j
-    __shared__ float sB[C];
-    __shared__ __align__(16) float sELC[D];       // exp(Lam_C) per key channel
+template <int V, int D, typename T, int NW, int NIT, int NE>
+struct WyShape {
+    static constexpr int NTH = 64 * NW;           // threads per workgroup
+    static constexpr int ROWS = 16 * NW * NIT;    // value rows per workgroup
+    static constexpr int NS = D / ROWS;           // workgroups per pair
+    static constexpr int NM = D / 16;             // 16-column blocks
+    static constexpr int KS = D + 4;              // padded LDS row stride of Y (floats)
+    static constexpr bool PK = V != GDN;          // per-key decays
+    static_assert(NS >= 1 && NS * ROWS == D, "the rows of a pair split evenly");
+    static_assert(NM % NW == 0, "Y's column blocks split evenly over the waves");
+    static_assert(NE == 1 || NE == 2 || NE == 4, "chunks of 16 entries: L <= 16 NE");
+};
 
-    size_t pair;
-    int n;
-    if (!resolve_merge_pair(P, slot_idx, mode, pair, n))
-        return;
+// LDS carve-up of the WY merge for logs of up to L entries.
+struct WyPlan {
+    int off_k;     // keys, [L][D] in the input dtype
+    int off_lam;   // per-key decays: Lam, [L][D] fp32
+    int off_t;     // packed columns of R
+    int off_f;     // per entry: beta_j (head-wise decay: times D(j, c)), 64 floats
+    int off_e;     // per entry (head-wise decay): E_j, 64 floats
+    int off_ec;    // E_c per key channel, D floats
+    int off_y;     // one chunk of Y: 16 rows of D + 4 floats
+    int off_n;     // the fill count read by the workgroup
+    int bytes;
+};
+
+__host__ __device__ inline WyPlan wy_plan(int variant, int D, int esize, int L) {
+    WyPlan p;
+    p.off_k = 0;
+    p.off_lam = round_up(L * D * esize, 256);
+    p.off_t = p.off_lam + (variant == DL_GDN ? 0 : round_up(L * D * 4, 256));
+    p.off_f = p.off_t + round_up(packed_t_len(variant, L) * 4, 256);
+    p.off_e = p.off_f + 256;
+    p.off_ec = p.off_e + 256;
+    p.off_y = p.off_ec + D * 4;
+    p.off_n = p.off_y + 16 * (D + 4) * 4;
+    p.bytes = p.off_n + 16;
+    return p;
+}
+
+template <int V, int D, typename T, bool NTS, int NW, int NIT, int NE>
+__global__ void __launch_bounds__(64 * NW, (NIT == 2 ? 4 : 1))
+merge_wy_kernel(Params P, const int *__restrict__ slot_idx, int mode, int npairs) {
+    using WS = WyShape<V, D, T, NW, NIT, NE>;
+    constexpr int NM = WS::NM, KS = WS::KS, NTH = WS::NTH;
+    constexpr bool PK = WS::PK, DELTA = V != RWKV6;
+    extern __shared__ __align__(16) unsigned char smem[];
     const int L = P.L;
+    const WyPlan wp = wy_plan(V, D, (int)sizeof(T), L);
+    const T *sk = reinterpret_cast<const T *>(smem + wp.off_k);
+    const float *slam = reinterpret_cast<const float *>(smem + wp.off_lam);
+    const float *sT = reinterpret_cast<const float *>(smem + wp.off_t);
+    float *sf = reinterpret_cast<float *>(smem + wp.off_f);
+    float *se = reinterpret_cast<float *>(smem + wp.off_e);
+    float *sec = reinterpret_cast<float *>(smem + wp.off_ec);
+    float *sy = reinterpret_cast<float *>(smem + wp.off_y);
+    int *sn = reinterpret_cast<int *>(smem + wp.off_n);
+
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int li = lane & 15, kg = lane >> 4;
-    float *Sp = P.base + pair * D * D;
-    const T *Kl = static_cast<const T *>(P.log_k) + pair * L * D;
-    const T *Vl = static_cast<const T *>(P.log_v) + pair * L * D;
-    const float *Gl = P.log_g + pair * L * ((V == GDN) ? 1 : D);
-    const float *Bl = P.log_beta + pair * L;
+    // block -> (pair, split): the NS workgroups of a pair are 8 blocks apart
+    const int xcd = blockIdx.x & 7, qb = blockIdx.x >> 3;
+    const int split = qb % WS::NS;
+    const int pr = (qb / WS::NS) * 8 + xcd;
+    if (pr >= npairs)
+        return;
+    const int H = P.heads;
+    const int r = pr / H, h = pr - r * H;
+    const int unit = slot_idx ? slot_idx[r] : r;
+    if (unit < 0 || unit >= P.units) {
+        if (split == 0)
+            reject_row(P, nullptr, D, DL_FLAG_BAD_SLOT);
+        return;
+    }
+    const size_t pair = (size_t)unit * H + h;
+    if (tid == 0) {
+        const int old = atomicAdd(P.fill + pair, 1 << 16);
+        const int n0 = old & 0xffff;
+        const bool go = n0 > 0 && n0 <= L && (mode != DL_MERGE_FULL || n0 == L);
+        if ((old >> 16) == WS::NS - 1)
+            P.fill[pair] = go ? 0 : n0;
+        sn[0] = go ? n0 : 0;
+    }
+    __syncthreads();
+    const int n = sn[0];
+    if (n == 0)
+        return;
+    const int nch = (n + 15) >> 4;       // chunks of 16 entries
+    const size_t e0 = pair * L;
 
-    // base rows in MFMA operand layout: st[it][m][e] = S[16 (wave NIT + it) + li][4 kg + 16 m + e]
+    // ---- loads, in the order they are needed: per-entry scalars (wave 0),
+    //      the staging of keys, decays and R, the base rows, chunk 0's values
+    float b_j = 1.f, lam_j = 0.f;
+    if (wave == 0 && lane < n) {
+        if constexpr (DELTA)
+            b_j = P.log_beta[e0 + lane];
+        if constexpr (!PK)
+            lam_j = P.log_g[e0 + lane];
+    }
+    {
+        const int nk = n * D * (int)sizeof(T) / 16;
+        const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_k) + e0 * D);
+        for (int b = 64 * wave; b < nk; b += NTH)
+            if (b + lane < nk)
+                load_to_lds<16>(ks + b + lane, smem + wp.off_k + 16 * b);
+        if constexpr (PK) {
+            const int nl = n * D / 4;
+            const float4 *ls = reinterpret_cast<const float4 *>(P.log_g + e0 * D);
+            for (int b = 64 * wave; b < nl; b += NTH)
+                if (b + lane < nl)
+                    load_to_lds<16>(ls + b + lane, smem + wp.off_lam + 16 * b);
+        }
+        if constexpr (DELTA) {
+            const int nt = n * (n - 1) / 2;
+            const float *ts = P.log_t + pair * packed_t_len(V, L);
+            for (int b = 64 * wave; b < nt; b += NTH)
+                if (b + lane < nt)
+                    load_to_lds<4>(ts + b + lane, smem + wp.off_t + 4 * b);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    float *Sp = P.base + pair * D * D;
+    const int row0 = split * WS::ROWS;
     floatx4 st[NIT][NM];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-        const int row = 16 * (wave * NIT + it) + li;
+        const int row = row0 + 16 * (wave * NIT + it) + li;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const float4 x = load_state4<NT>(Sp + (size_t)row * D + 4 * kg + 16 * m);
+            const float4 x = load_state4<NTS>(Sp + (size_t)row * D + 4 * kg + 16 * m);
             st[it][m] = floatx4{x.x, x.y, x.z, x.w};
         }
     }
-
-    for (int j0 = 0; j0 < n; j0 += C) {
-        const int cnt = (n - j0) < C ? (n - j0) : C;
-        // this chunk's logged values for the Z tiles (clamped, branch-free loads)
-        floatx4 vv[NIT];
+    // values of chunk c on this lane: V[entry 16 c + 4 kg + rr][row] (0 past n)
+    const T *Vl = static_cast<const T *>(P.log_v) + e0 * D;
+    auto load_values = [&](int c, floatx4 (&vv)[NIT]) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
-            const int row = 16 * (wave * NIT + it) + li;
+            const int row = row0 + 16 * (wave * NIT + it) + li;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int j = 4 * kg + r;
-                const float x = Elem<T>::load1(Vl + (size_t)(j0 + (j < cnt ? j : cnt - 1)) * D + row);
-                vv[it][r] = (j < cnt) ? x : 0.f;
+            for (int rr = 0; rr < 4; ++rr) {
+                const int j = 16 * c + 4 * kg + rr;
+                const float x = Elem<T>::load1(Vl + (size_t)(j < n ? j : n - 1) * D + row);
+                vv[it][rr] = j < n ? x : 0.f;
             }
         }
-        __syncthreads();   // the previous chunk's LDS operands are consumed
+    };
+    floatx4 vv[NIT];
+    load_values(0, vv);
+    __builtin_amdgcn_sched_barrier(0);
+    // the staging has landed once at most the base and value loads are outstanding
+    barrier_after_staging<NIT * (NM + 4)>();    // staged keys, decays and R
 
-        // ---- phase 1: keys of the chunk (zeros past cnt) and the decay
-        //      accumulated since the chunk's start, Lam_j - Lam_{j0-1} (the log
-        //      stores Lam since its first entry; entries past cnt repeat the
-        //      last one, so their decay adds nothing)
-        for (int idx = tid; idx < C * (D / 4); idx += 256) {
-            const int j = idx / (D / 4), c = 4 * (idx - j * (D / 4));
-            const int e = j0 + (j < cnt ? j : cnt - 1);
-            float4 kv = Elem<T>::load4(Kl + (size_t)e * D + c);
-            float4 lv, lb = make_float4(0.f, 0.f, 0.f, 0.f);
-            if constexpr (V == GDN) {
-                lv = make_float4(Gl[e], Gl[e], Gl[e], Gl[e]);
-                if (j0 > 0)
-                    lb = make_float4(Gl[j0 - 1], Gl[j0 - 1], Gl[j0 - 1], Gl[j0 - 1]);
+    // ---- per-entry factors and E_c
+    if (wave == 0) {
+        if constexpr (!PK) {
+            const float lam_c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_j), n - 1));
+            if (lane < n) {
+                sf[lane] = b_j * fast_exp(lam_c - lam_j);
+                se[lane] = fast_exp(lam_j);
+            }
+            const float ec = fast_exp(lam_c);
+            for (int c = lane; c < D; c += 64)
+                sec[c] = ec;
+        } else {
+            if (lane < n)
+                sf[lane] = b_j;
+            for (int c = lane; c < D; c += 64)
+                sec[c] = fast_exp(slam[(n - 1) * D + c]);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase A: z_c = V_c^T - S0 Kt_c^T (MFMA, accumulator initialised
+    //      with the values): z[c][it][rr] = Z[row][entry 16 c + 4 kg + rr]
+    floatx4 z[NE][NIT];
+#pragma unroll
+    for (int c = 0; c < NE; ++c) {
+        if (c >= nch)
+            break;
+        floatx4 vn[NIT];
+        if (c + 1 < nch)
+            load_values(c + 1, vn);      // the next chunk's values, in flight
+#pragma unroll
+        for (int it = 0; it < NIT; ++it)
+            z[c][it] = vv[it];
+        if constexpr (DELTA) {
+            const int j = 16 * c + li;            // this lane's entry of the A operand
+            const bool live = j < n;
+            const int jc = live ? j : n - 1;
+            const float ej = PK ? 1.f : (live ? se[jc] : 0.f);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (m % 2 == 0)
+                    __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
+                const int col = 4 * kg + 16 * m;
+                float4 kt = lds_load4<T>(reinterpret_cast<const unsigned char *>(sk), jc * D + col);
+                if constexpr (PK) {
+                    const float4 l4 = *reinterpret_cast<const float4 *>(slam + jc * D + col);
+                    kt.x *= fast_exp(l4.x), kt.y *= fast_exp(l4.y);
+                    kt.z *= fast_exp(l4.z), kt.w *= fast_exp(l4.w);
+                }
+                const float s = live ? -ej : 0.f;   // -Kt (head-wise: E_j; per-key: folded above)
+                const float f = PK ? (live ? -1.f : 0.f) : s;
+                const float a0 = f * kt.x, a1 = f * kt.y, a2 = f * kt.z, a3 = f * kt.w;
+#pragma unroll
+                for (int it = 0; it < NIT; ++it) {
+                    z[c][it] = mfma16x16x4(a0, st[it][m][0], z[c][it]);
+                    z[c][it] = mfma16x16x4(a1, st[it][m][1], z[c][it]);
+                    z[c][it] = mfma16x16x4(a2, st[it][m][2], z[c][it]);
+                    z[c][it] = mfma16x16x4(a3, st[it][m][3], z[c][it]);
+                }
+            }
+        }
+        if (c + 1 < nch)
+#pragma unroll
+            for (int it = 0; it < NIT; ++it)
+                vv[it] = vn[it];
+    }
+
+    // ---- phase B: S0 diag(E_c), then S0 += z_c Y_c chunk by chunk
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const float4 el = *reinterpret_cast<const float4 *>(sec + 4 * kg + 16 * m);
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            st[it][m][0] *= el.x;
+            st[it][m][1] *= el.y;
+            st[it][m][2] *= el.z;
+            st[it][m][3] *= el.w;
+        }
+    }
+    // Q[i][ch] = f_i k_i[ch] (per-key: times D(i, c) on the channel); 0 past n
+    auto qval = [&](int i, int ch) {
+        const int ic = i < n ? i : n - 1;
+        float q = Elem<T>::load1(sk + ic * D + ch) * sf[ic];
+        if constexpr (PK)
+            q *= fast_exp(slam[(n - 1) * D + ch] - slam[ic * D + ch]);
+        return i < n ? q : 0.f;
+    };
+#pragma unroll
+    for (int c = 0; c < NE; ++c) {
+        if (c >= nch)
+            break;
+        const int j0 = 16 * c;
+        if (c > 0)
+            __syncthreads();    // the previous chunk's Y is consumed
+        // Y_c = R_c Q on this wave's column blocks: Y[j0 + 4 kg + rr][16 m + li]
+#pragma unroll
+        for (int mb = 0; mb < NM / NW; ++mb) {
+            const int m = wave * (NM / NW) + mb;
+            const int ch = 16 * m + li;
+            floatx4 y = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (DELTA) {
+                const int j = j0 + li;                 // this lane's row of R
+                for (int i0 = j0; i0 < n; i0 += 4) {
+                    const int i = i0 + kg;
+                    // R[j][i]: 1 on the diagonal, column i's packed entry above it
+                    float rji = (i == j) ? 1.f : 0.f;
+                    if (j < i && i < n)
+                        rji = sT[i * (i - 1) / 2 + j];
+                    rji = (j < n) ? rji : 0.f;
+                    y = mfma16x16x4(rji, qval(i, ch), y);
+                }
             } else {
-                lv = *reinterpret_cast<const float4 *>(Gl + (size_t)e * D + c);
-                if (j0 > 0)
-                    lb = *reinterpret_cast<const float4 *>(Gl + (size_t)(j0 - 1) * D + c);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    y[rr] = qval(j0 + 4 * kg + rr, ch);
             }
-            if (j >= cnt)
-                kv = make_float4(0.f, 0.f, 0.f, 0.f);
-            const float4 lam = make_float4(lv.x - lb.x, lv.y - lb.y, lv.z - lb.z, lv.w - lb.w);
-            *reinterpret_cast<float4 *>(&sK[j * KS + c]) = kv;
-            *reinterpret_cast<float4 *>(&sLam[j * KS + c]) = lam;
-            *reinterpret_cast<float4 *>(&sKt[j * KS + c]) =
-                make_float4(kv.x * expf(lam.x), kv.y * expf(lam.y), kv.z * expf(lam.z), kv.w * expf(lam.w));
-            if (j == C - 1)
-                *reinterpret_cast<float4 *>(&sELC[c]) =
-                    make_float4(expf(lam.x), expf(lam.y), expf(lam.z), expf(lam.w));
-        }
-        if (tid < C) {
-            const int e = j0 + (tid < cnt ? tid : cnt - 1);
-            sB[tid] = (V != RWKV6 && tid < cnt) ? Bl[e] : 0.f;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                sy[(4 * kg + rr) * KS + ch] = y[rr];
         }
         __syncthreads();
-
-        // ---- phase 2: Gram with pairwise decay, two lanes per pair (i < j), halves of the channels
-        if constexpr (V != RWKV6) {
-            const int p = tid >> 1, half = tid & 1;
-            int i = 0, j = 1;
-            const bool inpair = p < C * (C - 1) / 2;
-            if (inpair) {
-                int base = 0;
-                while (base + j <= p) {
-                    base += j;
-                    ++j;
-                }
-                i = p - base;
-            }
-            const bool valid = inpair && j < cnt;
-            float gsum = 0.f;
-            if (valid) {
-                const int c0 = half * (D / 2);
-#pragma unroll 2
-                for (int c = c0; c < c0 + D / 2; c += 4) {
-                    const float4 a = *reinterpret_cast<const float4 *>(&sK[i * KS + c]);
-                    const float4 b = *reinterpret_cast<const float4 *>(&sK[j * KS + c]);
-                    if constexpr (V == GDN) {
-                        gsum += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
-                    } else {
-                        const float4 l1 = *reinterpret_cast<const float4 *>(&sLam[i * KS + c]);
-                        const float4 l2 = *reinterpret_cast<const float4 *>(&sLam[j * KS + c]);
-                        gsum += a.x * b.x * expf(l2.x - l1.x) + a.y * b.y * expf(l2.y - l1.y) +
-                                a.z * b.z * expf(l2.z - l1.z) + a.w * b.w * expf(l2.w - l1.w);
-                    }
-                }
-            }
-            gsum += dpp_mov<0xB1>(gsum);   // add the other half (adjacent lane)
-            if (V == GDN && valid)
-                gsum *= expf(sLam[j * KS] - sLam[i * KS]);
-            if (inpair && half == 0)
-                sM[i * C + j] = valid ? sB[j] * gsum : 0.f;
-        }
-        __syncthreads();
-
-        // ---- phase 3: Y = diag(beta) (I + M)^{-1} Kh, Kh_j = k_j exp(Lam_C - Lam_j)
-        if (tid < D) {
-            const int c = tid;
-            const float lamC = sLam[(C - 1) * KS + c];
-            float x[C];
-#pragma unroll
-            for (int j = C - 1; j >= 0; --j) {
-                __builtin_amdgcn_sched_barrier(0);   // keep this row's LDS reads from being hoisted
-                float kh = sK[j * KS + c] * expf(lamC - sLam[j * KS + c]);
-                if constexpr (V != RWKV6) {
-#pragma unroll
-                    for (int m = j + 1; m < C; ++m)
-                        kh -= sM[j * C + m] * x[m];
-                    x[j] = kh;
-                    sY[j * KS + c] = sB[j] * kh;
-                } else {
-                    sY[j * KS + c] = kh;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- W^T = Kt S^T (MFMA); Z^T = V^T - W^T: z[it][r] = Z[row 16 (wave NIT + it) + li][entry 4 kg + r]
-        floatx4 z[NIT];
-#pragma unroll
-        for (int it = 0; it < NIT; ++it) {
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (V != RWKV6) {
-#pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    if (m % 2 == 0)
-                        __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
-                    const float4 a = *reinterpret_cast<const float4 *>(&sKt[li * KS + 4 * kg + 16 * m]);
-                    acc = mfma16x16x4(a.x, st[it][m][0], acc);
-                    acc = mfma16x16x4(a.y, st[it][m][1], acc);
-                    acc = mfma16x16x4(a.z, st[it][m][2], acc);
-                    acc = mfma16x16x4(a.w, st[it][m][3], acc);
-                }
-            }
-            z[it] = vv[it] - acc;
-        }
-        // ---- S'^T = diag(exp Lam_C) S^T + Y^T Z^T (MFMA, accumulating in place)
+        // S'^T += Y_c^T z_c^T (MFMA, accumulating in place)
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             if (m % 2 == 0)
                 __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
-            const float4 el = *reinterpret_cast<const float4 *>(&sELC[4 * kg + 16 * m]);
             float a[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                a[r] = sY[(4 * kg + r) * KS + 16 * m + li];
+            for (int rr = 0; rr < 4; ++rr)
+                a[rr] = sy[(4 * kg + rr) * KS + 16 * m + li];
 #pragma unroll
-            for (int it = 0; it < NIT; ++it) {
-                floatx4 acc = st[it][m];
-                acc[0] *= el.x;
-                acc[1] *= el.y;
-                acc[2] *= el.z;
-                acc[3] *= el.w;
+            for (int it = 0; it < NIT; ++it)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc = mfma16x16x4(a[r], z[it][r], acc);
-                st[it][m] = acc;
-            }
+                for (int rr = 0; rr < 4; ++rr)
+                    st[it][m] = mfma16x16x4(a[rr], z[c][it][rr], st[it][m]);
         }
     }
 
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-        const int row = 16 * (wave * NIT + it) + li;
+        const int row = row0 + 16 * (wave * NIT + it) + li;
 #pragma unroll
         for (int m = 0; m < NM; ++m)
-            store_state4<NT>(Sp + (size_t)row * D + 4 * kg + 16 * m,
-                          make_float4(st[it][m][0], st[it][m][1], st[it][m][2], st[it][m][3]));
+            store_state4<NTS>(Sp + (size_t)row * D + 4 * kg + 16 * m,
+                              make_float4(st[it][m][0], st[it][m][1], st[it][m][2], st[it][m][3]));
     }
-    if (tid == 0)
-        P.fill[pair] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -376,15 +483,39 @@ static hipError_t replay_t(const Params &P, int rows, const int *slot_idx, int m
     return hipGetLastError();
 }
 
+template <int V, int D, typename T, int NW, int NIT, int NE>
+static void wy_launch(const Params &P, int pairs, const int *slot_idx, int mode, const Launch &ln) {
+    using WS = WyShape<V, D, T, NW, NIT, NE>;
+    const WyPlan wp = wy_plan(V, D, (int)sizeof(T), P.L);
+    const dim3 grid(((pairs + 7) / 8) * 8 * WS::NS), block(WS::NTH);
+    if (P.stream)
+        hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T, true, NW, NIT, NE>), grid, block, wp.bytes,
+                              ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode, pairs);
+    else
+        hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T, false, NW, NIT, NE>), grid, block, wp.bytes,
+                              ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode, pairs);
+}
+
+// One workgroup per pair, holding the pair's whole base, while the chunks'
+// z tiles fit beside it in registers (logs of up to 32 entries at d = 128);
+// longer logs split a pair's rows over two workgroups.  (Splitting further,
+// to spread launches over few pairs across more CUs, measured slower: a
+// workgroup's time is set by its chain of loads, barriers and contractions,
+// not by its share of the base.)
 template <int V, int D, typename T>
 static hipError_t wy_t(const Params &P, int rows, const int *slot_idx, int mode,
                        const Launch &ln) {
-    if (P.stream)
-        hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T, true>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start,
-                              ln.stop, 0, P, slot_idx, mode);
-    else
-        hipExtLaunchKernelGGL((merge_wy_kernel<V, D, T, false>), dim3(rows * P.heads), dim3(256), 0, ln.stream, ln.start,
-                              ln.stop, 0, P, slot_idx, mode);
+    const int pairs = rows * P.heads;
+    if constexpr (D == 128) {
+        if (P.L <= 16)
+            wy_launch<V, D, T, 4, 2, 1>(P, pairs, slot_idx, mode, ln);
+        else if (P.L <= 32)
+            wy_launch<V, D, T, 4, 2, 2>(P, pairs, slot_idx, mode, ln);
+        else
+            wy_launch<V, D, T, 4, 1, 4>(P, pairs, slot_idx, mode, ln);
+    } else {
+        wy_launch<V, D, T, 4, 1, 4>(P, pairs, slot_idx, mode, ln);
+    }
     return hipGetLastError();
 }
 

@@ -210,6 +210,28 @@ def merging_order(batch: int, merging, spread: bool):
     return np.insert(rest, np.arange(len(merging)) * gap, merging)
 
 
+ORDERS = ("auto", "natural", "first", "spread", "lpt")
+
+
+def row_order(policy: str, fills: np.ndarray, L: int, wy: bool):
+    """Dispatch order of a step's rows given each sequence's log fill before
+    the step (all sequences active), or None for input order.  The rows whose
+    log the step fills merge in place and run longer: "first" puts them
+    ahead of the rest, "spread" spaces them evenly through the batch, "lpt"
+    sorts every row by the work it has (merging rows, then the fullest logs
+    first); "auto" is "first" for the compact-WY log, whose in-step merge is
+    the longer one, and "spread" for the factor log."""
+    batch = len(fills)
+    merging = np.nonzero(fills + 1 == L)[0]
+    if policy == "auto":
+        policy = "first" if wy else "spread"
+    if policy == "natural" or not (0 < len(merging) < batch):
+        return None
+    if policy == "lpt":
+        return np.argsort(-fills, kind="stable")
+    return merging_order(batch, merging, spread=policy == "spread")
+
+
 def parse_args(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,9 +247,13 @@ def parse_args(argv=None):
                     help="eager; log (merge launched after the step that fills a log); "
                          "log-fused (that step merges in the same pass); af, af-fused: "
                          "the same with the additive-factor log (delta-rule variants)")
+    ap.add_argument("--order", default="auto", choices=ORDERS,
+                    help="dispatch order of the rows of steps that merge in place (ragged logs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
+    ap.add_argument("--library", default=None, metavar="PATH",
+                    help="load this build of libdeltalog.so instead of the package's")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args(argv)
@@ -281,7 +307,10 @@ def main(argv=None):
     from linear_attention_recurrent_gated_amd import binding as B
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    B.load()
+    if args.library:
+        B.load(args.library)
+    else:
+        B.load()
     dev = torch.device("cuda:0")
     wl = W.WORKLOADS[args.config]
     L = args.L or (16 if args.config == 3 else wl.log_lens[0])
@@ -406,11 +435,12 @@ def main(argv=None):
             # batch for the factor log; inputs and outputs stay in batch order
             full_next = np.nonzero(fills + np.isin(np.arange(Bt), act[tau]) == L)[0]
             order_p = None
-            if wl.ragged and tau >= prefix and fused and 0 < len(full_next) < Bt:
-                order = merging_order(Bt, full_next, spread=path.startswith("af"))
-                order_t = torch.from_numpy(order.astype(np.int32)).to(dev)
-                keep.append(order_t)
-                order_p = order_t.data_ptr()
+            if wl.ragged and tau >= prefix and fused:
+                order = row_order(args.order, fills, L, wy=not path.startswith("af"))
+                if order is not None:
+                    order_t = torch.from_numpy(order.astype(np.int32)).to(dev)
+                    keep.append(order_t)
+                    order_p = order_t.data_ptr()
             merge_slots = None
             if wl.ragged and separate and len(full_next):
                 merge_slots = torch.from_numpy(full_next.astype(np.int32)).to(dev)
@@ -569,7 +599,8 @@ def main(argv=None):
     out["config"] = {"workload": wl.name, "variant": W.VARIANT_NAMES[wl.variant],
                      "batch": Bt, "layers": layers, "heads": H, "d_k": d, "d_v": wl.d_v,
                      "log_len": L, "input_dtype": wl.dtype, "state_dtype": "fp32",
-                     "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix}
+                     "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix,
+                     "row_order": args.order}
     if args.warmup is not None and Wu != args.warmup:
         out["warmup_requested"] = args.warmup
     # merges inside the timed window: steps at which some log fills, and the

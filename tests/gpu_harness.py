@@ -121,10 +121,10 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
             for path in paths:
                 o_full = torch.zeros((wl.units_total, H, d), dtype=torch.float32, device="cuda")
                 order = None
-                if bench_schedule and path.endswith("-fused") and len(act) == Bt \
-                        and 0 < len(full_next) < Bt:
-                    order = torch.from_numpy(bench.merging_order(
-                        Bt, full_next, spread=path.startswith("af")).astype(np.int32)).cuda()
+                if bench_schedule and path.endswith("-fused") and len(act) == Bt:
+                    o_np = bench.row_order("auto", fills, L, wy=not path.startswith("af"))
+                    if o_np is not None:
+                        order = torch.from_numpy(o_np.astype(np.int32)).cuda()
                 for l in range(layers):
                     st = states[path][l]
                     lo, hi = l * Bt, (l + 1) * Bt

@@ -146,3 +146,24 @@ def test_default_workload_is_the_largest():
     assert states == 4 * 2**30 and all(
         w.units_total * w.heads * w.d_k * w.d_v <= wl.units_total * wl.heads * wl.d_k * wl.d_v
         for w in W.WORKLOADS.values())
+
+
+@pytest.mark.parametrize("policy", bench.ORDERS)
+def test_row_order_policies(policy):
+    rng = np.random.default_rng(5)
+    L = 32
+    fills = rng.integers(0, L, size=256)
+    order = bench.row_order(policy, fills, L, wy=False)
+    if policy == "natural":
+        assert order is None
+        return
+    assert sorted(order.tolist()) == list(range(256))
+    merging = np.nonzero(fills == L - 1)[0]
+    pos = np.argsort(order)[merging]                       # where the merging rows go
+    if policy in ("first", "lpt"):
+        assert np.array_equal(np.sort(pos), np.arange(len(merging)))
+    if policy == "lpt":
+        assert np.all(np.diff(fills[order]) <= 0)
+    # nothing to order when no row (or every row) merges
+    assert bench.row_order(policy, np.zeros(8, dtype=np.int64), L, wy=True) is None
+    assert bench.row_order(policy, np.full(8, L - 1), L, wy=True) is None

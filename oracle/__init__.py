@@ -13,13 +13,20 @@ falls back to it.
   additive-factor log stores (numpy, float64).
 * :mod:`oracle.exact` -- exact rational (``fractions.Fraction``) models used
   to pin the float64 oracle and the deferred base + log algebra.
+* :mod:`oracle.quant` -- a base kept in INT8 with fp32 key channels (a
+  reading of the DAMP abstract): the quantiser, its inverse, and the
+  recurrence that re-quantises the base at every merge.
 
 Parity status: every function here is pinned by the CPU tests:
 :func:`run` and :func:`additive_factor` in ``tests/test_oracle_pins.py``
 (brute-force product expansion, the delta-rule write invariant, the identity
 case, closed forms and the exact equality of eager and deferred schedules),
 :func:`readout` in ``tests/test_oracle_readout.py`` (the recurrence's own last
-output and a hand-worked example, with planted mistakes that must fail).  The pages print no worked numeric
+output and a hand-worked example, with planted mistakes that must fail),
+:mod:`oracle.quant` in ``tests/test_oracle_quant.py`` (grid values, ties to
+even, the rounding error bound, zero rows and kept outliers, planted
+quantiser mistakes; the mixed recurrence against the plain one and against
+the deferred log's schedule model).  The pages print no worked numeric
 example, so no stored value comes from them.
 """
 from __future__ import annotations
@@ -50,6 +57,8 @@ def _load(path: str | None = None):
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_int,
         ]
+        lib.oracle_run_f64_state.restype = ctypes.c_int
+        lib.oracle_run_f64_state.argtypes = lib.oracle_run.argtypes
         lib.oracle_max_threads.restype = ctypes.c_int
         _libs[key] = lib
     return _libs[key]
@@ -80,7 +89,7 @@ def _ptr(a):
 
 
 def run(variant: int, q, k, v, g, beta=None, S0=None, t_start=None, threads: int | None = None,
-        lib_path: str | None = None):
+        lib_path: str | None = None, S0_f64=None):
     """Run the recurrence for ``P`` independent states over ``T`` steps.
 
     Shapes: ``q, k`` ``[T, P, d_k]``; ``v`` ``[T, P, d_v]``; ``g`` ``[T, P]``
@@ -89,6 +98,8 @@ def run(variant: int, q, k, v, g, beta=None, S0=None, t_start=None, threads: int
     then write gate -- for the gated form); ``S0`` ``[P, d_v, d_k]`` or None for
     zeros; ``t_start`` ``[P]`` first step each state takes (outputs before it
     are zero).  All float inputs are the exact values the kernels consume.
+    ``S0_f64`` ``[P, d_v, d_k]`` float64 replaces ``S0`` when the initial state
+    is not an fp32 value (a dequantised base).
 
     Returns ``(o, S)``: float64 ``[T, P, d_v]`` and ``[P, d_v, d_k]``.
     """
@@ -114,7 +125,15 @@ def run(variant: int, q, k, v, g, beta=None, S0=None, t_start=None, threads: int
         assert ts.shape == (P,)
     o = np.zeros((T, P, dv), dtype=np.float64)
     S = np.zeros((P, dv, dk), dtype=np.float64)
-    rc = _load(lib_path).oracle_run(variant, P, dk, dv, T, _ptr(S0), _ptr(q), _ptr(k), _ptr(v),
+    lib = _load(lib_path)
+    if S0_f64 is not None:
+        S0d = np.ascontiguousarray(S0_f64, dtype=np.float64)
+        assert S0d.shape == (P, dv, dk)
+        rc = lib.oracle_run_f64_state(variant, P, dk, dv, T, _ptr(S0d), _ptr(q), _ptr(k), _ptr(v),
+                                      _ptr(g), _ptr(beta), _ptr(ts), _ptr(o), _ptr(S),
+                                      int(threads or default_threads()))
+    else:
+        rc = lib.oracle_run(variant, P, dk, dv, T, _ptr(S0), _ptr(q), _ptr(k), _ptr(v),
                             _ptr(g), _ptr(beta), _ptr(ts), _ptr(o), _ptr(S),
                             int(threads or default_threads()))
     if rc != 0:

@@ -86,9 +86,9 @@ static void add_outer(int dv, int dk, double *S, double c, const double *a, cons
 
 /* One state through steps t_first..T-1. */
 static void run_one(int variant, int64_t pair, int64_t n_pairs, int dk, int dv, int T,
-                    int t_first, const float *S0, const float *q, const float *k,
-                    const float *v, const float *g, const float *beta, double *o,
-                    double *S_out, double *work)
+                    int t_first, const float *S0, const double *S0d, const float *q,
+                    const float *k, const float *v, const float *g, const float *beta,
+                    double *o, double *S_out, double *work)
 {
     double *S = S_out + (size_t)pair * dv * dk;
     double *qd = work;            /* d_k */
@@ -101,7 +101,8 @@ static void run_one(int variant, int64_t pair, int64_t n_pairs, int dk, int dv, 
     double *wv = ek + dk;         /* d_v */
 
     for (size_t e = 0; e < (size_t)dv * dk; ++e)
-        S[e] = S0 ? (double)S0[(size_t)pair * dv * dk + e] : 0.0;
+        S[e] = S0d ? S0d[(size_t)pair * dv * dk + e]
+             : S0  ? (double)S0[(size_t)pair * dv * dk + e] : 0.0;
 
     for (int t = 0; t < T; ++t) {
         double *o_t = o + ((size_t)t * n_pairs + pair) * dv;
@@ -179,10 +180,37 @@ static void run_one(int variant, int64_t pair, int64_t n_pairs, int dk, int dv, 
  *
  * Returns 0, or -1 for invalid arguments, -2 if scratch memory is unavailable.
  */
+static int run_all(int variant, int64_t n_pairs, int d_k, int d_v, int T, const float *S0,
+                   const double *S0d, const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, const int32_t *t_start, double *o,
+                   double *S_out, int n_threads);
+
 int oracle_run(int variant, int64_t n_pairs, int d_k, int d_v, int T, const float *S0,
                const float *q, const float *k, const float *v, const float *g,
                const float *beta, const int32_t *t_start, double *o, double *S_out,
                int n_threads)
+{
+    return run_all(variant, n_pairs, d_k, d_v, T, S0, NULL, q, k, v, g, beta, t_start, o,
+                   S_out, n_threads);
+}
+
+/* The same with a float64 initial state S0d [n_pairs, d_v, d_k] (a state
+ * that is not an fp32 value, e.g. a dequantised base). */
+int oracle_run_f64_state(int variant, int64_t n_pairs, int d_k, int d_v, int T,
+                         const double *S0d, const float *q, const float *k, const float *v,
+                         const float *g, const float *beta, const int32_t *t_start, double *o,
+                         double *S_out, int n_threads)
+{
+    if (!S0d)
+        return -1;
+    return run_all(variant, n_pairs, d_k, d_v, T, NULL, S0d, q, k, v, g, beta, t_start, o,
+                   S_out, n_threads);
+}
+
+static int run_all(int variant, int64_t n_pairs, int d_k, int d_v, int T, const float *S0,
+                   const double *S0d, const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, const int32_t *t_start, double *o,
+                   double *S_out, int n_threads)
 {
     if (variant < ORACLE_GDN || variant > ORACLE_GDN2 || n_pairs < 0 || d_k <= 0 ||
         d_v <= 0 || T < 0 || !q || !k || !v || !g || !o || !S_out)
@@ -211,7 +239,8 @@ int oracle_run(int variant, int64_t n_pairs, int d_k, int d_v, int T, const floa
             if (!work)
                 continue;
             const int t0 = t_start ? t_start[p] : 0;
-            run_one(variant, p, n_pairs, d_k, d_v, T, t0, S0, q, k, v, g, beta, o, S_out, work);
+            run_one(variant, p, n_pairs, d_k, d_v, T, t0, S0, S0d, q, k, v, g, beta, o, S_out,
+                    work);
         }
         free(work);
     }

@@ -79,10 +79,16 @@ def byte_model(wl: W.Workload):
     return dict(St=St, In=In, Out=Out, E=E, R=R, E_af=E_af)
 
 
-def form_model(m, path):
-    """The byte model of the log form a path uses."""
+KEPT_CHANNELS = 8      # INT8-base paths: key channels per head kept in fp32
+
+
+def form_model(m, path, d=None):
+    """The byte model of the log form a path uses; "-i8" paths read and write
+    an INT8 base (codes, a row scale, KEPT_CHANNELS fp32 values per row)."""
     if path.startswith("af"):
-        return dict(m, E=m["E_af"], R=0)
+        m = dict(m, E=m["E_af"], R=0)
+    if path.endswith("-i8"):
+        m = dict(m, St=d * d + 4 * d * (1 + KEPT_CHANNELS))
     return m
 
 
@@ -243,10 +249,13 @@ def parse_args(argv=None):
     ap.add_argument("--reps", type=int, default=3,
                     help="timed repetitions of the K steps (each from the same state); "
                          "value is the median")
-    ap.add_argument("--paths", default="eager,log,log-fused,af,af-fused",
+    ap.add_argument("--paths", default="eager,log,log-fused,af,af-fused,af-fused-i8",
                     help="eager; log (merge launched after the step that fills a log); "
                          "log-fused (that step merges in the same pass); af, af-fused: "
-                         "the same with the additive-factor log (delta-rule variants)")
+                         "the same with the additive-factor log (delta-rule variants); "
+                         "af-i8, af-fused-i8: the factor log over an INT8 base with fp32 "
+                         "kept channels (a quantised state: reported beside the exact "
+                         "paths, never as the headline)")
     ap.add_argument("--order", default="auto", choices=ORDERS,
                     help="dispatch order of the rows of steps that merge in place (ragged logs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -324,6 +333,7 @@ def main(argv=None):
     paths = args.paths.split(",")
     if not wl.has_beta:
         # the additive variant's log already stores additive factors: af == log
+        # (and the INT8 base is built for the delta-rule variants)
         paths = [p for p in paths if not p.startswith("af")]
     if wl.variant == W.GDN2:
         # the gated form's log is built in the factor form only
@@ -406,16 +416,23 @@ def main(argv=None):
 
     results = {}
     for path in paths:
-        m = form_model(m0, path)
-        fused = path.endswith("-fused")
-        separate = path in ("log", "af")          # merges launched after the step
+        m = form_model(m0, path, d)
+        q8 = path.endswith("-i8")
+        fused = "-fused" in path
+        separate = path in ("log", "af", "af-i8")     # merges launched after the step
         states = []
         for l in range(layers):
             st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype, device=dev,
                                merge_on_step=fused,
-                               log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY)
-            st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
+                               log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY,
+                               base_format=B.DL_BASE_I8 if q8 else B.DL_BASE_F32,
+                               kept_channels=KEPT_CHANNELS if q8 else 0)
+            if q8:
+                st.import_base(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]).to(dev))
+            else:
+                st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
             states.append(st)
+        kept_idx = states[0].kept_idx.cpu().numpy() if q8 else None
         O = torch.zeros((T, U, H, d), dtype=torch.float32, device=dev)
         stream = torch.cuda.current_stream().cuda_stream
         lib = B.load()
@@ -542,7 +559,7 @@ def main(argv=None):
                         if separate and full.any():   # a merge launch followed
                             idle = 0 if wl.ragged else (~full).sum()   # ragged: only full units launched
                             mbytes += layers * H * (merge_bytes(m, L) * full.sum() + 4 * idle)
-                            mflops += layers * H * merge_flops(wl, L, path == "af") * full.sum()
+                            mflops += layers * H * merge_flops(wl, L, path.startswith("af")) * full.sum()
                         f[full] = 0
         kern_s = sum(step_ms) / 1e3
         # the method's bytes (one figure for every log form): eager, or a DeltaLog
@@ -572,8 +589,10 @@ def main(argv=None):
         # sampled outputs and final states for the parity check
         su, sh = torch.from_numpy(sample // H).to(dev), torch.from_numpy(sample % H).to(dev)
         res["o_sample"] = O[:, su, sh].double().cpu().numpy()            # [T, n, d]
-        Sfull = torch.cat([st.base for st in states], 0)
+        Sfull = torch.cat([st.export_base() if q8 else st.base for st in states], 0)
         res["S_sample"] = Sfull[su, sh].double().cpu().numpy()
+        if q8:
+            res["kept_idx"] = kept_idx
         results[path] = res
         for st in states:
             st.close()
@@ -614,6 +633,7 @@ def main(argv=None):
     # fills a log or merged inside that step
     knames = {"log": "log_step_kernel", "log-fused": "log_step_kernel.fused",
               "af": "af_step_kernel", "af-fused": "af_step_kernel.fused"}
+    qnames = {"af-i8": "af_step_kernel.i8", "af-fused-i8": "af_step_kernel.fused.i8"}
     logs = [p for p in knames if p in results]
     main_path = max(logs, key=lambda p: results[p]["updates_per_s"]) if logs else paths[0]
     r = results[main_path]
@@ -669,6 +689,26 @@ def main(argv=None):
                            if ms else None}
     if merges:
         out["merge"] = merges
+    # the INT8-base paths: a quantised state, so never the headline; reported
+    # beside it with their own byte model
+    q8paths = []
+    for qp, kn in qnames.items():
+        if qp not in results:
+            continue
+        u = results[qp]
+        e = {"path": qp, "value": u["updates_per_s"], "ms_per_step": u["ms_per_step"],
+             "ms_per_step_range": [u["ms_per_step_min"], u["ms_per_step_max"]],
+             "kept_channels": KEPT_CHANNELS, "base_bits_per_value": 8 + 32 * (1 + KEPT_CHANNELS) / d,
+             "kernel": kn, "avg_launch_us": u["step_kernel_avg_us"],
+             "path_bytes_per_launch": u["step_bytes_per_launch"],
+             "achieved_GBps": u["step_kernel_GBps"], "frac": u["step_kernel_GBps"] / HBM_PEAK_GBPS}
+        if "eager" in results:
+            e["speedup_vs_eager"] = u["updates_per_s"] / results["eager"]["updates_per_s"]
+        if main_path in results and main_path in knames:
+            e["speedup_vs_fp32_deltalog"] = u["updates_per_s"] / results[main_path]["updates_per_s"]
+        q8paths.append(e)
+    if q8paths:
+        out["int8_base"] = q8paths
     if main_path in knames:
         # dense-state write traffic, eager over DeltaLog: the byte model, and the
         # counters (bytes written per launch) when both summaries match the sources
@@ -702,6 +742,8 @@ def main(argv=None):
                                          f"({n_upd} updates), float64"}
         parity = {}
         for path, res in results.items():
+            if path.endswith("-i8"):
+                continue
             o = res["o_sample"]
             scale_o = np.maximum(1.0, np.abs(o_ref).max(axis=(0, 2)))
             eo = (np.abs(o - o_ref).max(axis=(0, 2)) / scale_o).max()
@@ -709,6 +751,29 @@ def main(argv=None):
             es = (np.abs(res["S_sample"] - S_ref).reshape(len(sample), -1).max(axis=1) / scale_s).max()
             parity[path] = {"max_rel_err_outputs": float(eo), "max_rel_err_state": float(es),
                             "ok": bool(eo <= 2e-4 and es <= 2e-4)}
+        # INT8-base paths against the oracle's quantised-base recurrence (the
+        # base re-quantised at every merge), on the first 32 sampled states:
+        # informational, since a code that an fp32 state takes on the other
+        # side of a rounding boundary shifts that entry by one INT8 step
+        from oracle import quant
+        for path, res in results.items():
+            if not path.endswith("-i8"):
+                continue
+            n = min(32, len(sample))
+            kept = res["kept_idx"][sample[:n] % H]
+            o_q, _, fin = quant.run_quantized_base(
+                wl.variant, np.stack(sq)[:, :n], np.stack(sk)[:, :n], np.stack(sv)[:, :n],
+                np.stack(sg)[:, :n], np.stack(sb)[:, :n] if sb else None,
+                S0.reshape(P, d, d)[sample[:n]], t_start[:n], L, kept, threads=1)
+            o = res["o_sample"][:, :n]
+            scale_o = np.maximum(1.0, np.abs(o_q).max(axis=(0, 2)))
+            eo = (np.abs(o - o_q).max(axis=(0, 2)) / scale_o).max()
+            S_q = quant.dequantize_base(*fin, kept)
+            scale_s = np.maximum(1.0, np.abs(S_q).reshape(n, -1).max(axis=1))
+            es = (np.abs(res["S_sample"][:n] - S_q).reshape(n, -1).max(axis=1) / scale_s).max()
+            parity[path] = {"max_rel_err_outputs": float(eo), "max_rel_err_state": float(es),
+                            "reference": "oracle.quant.run_quantized_base", "states": n,
+                            "ok": bool(eo <= 2e-4)}
         out["parity"] = parity
     print(json.dumps(out), flush=True)
     return 0

@@ -65,7 +65,9 @@ typedef enum {
     DL_OK = 0,
     DL_ERR_INVALID = 1,      /* null or misaligned pointer, bad count, argument wrong for the variant */
     DL_ERR_UNSUPPORTED = 2,  /* well-formed but not built: d_k != d_v, d not in {64, 128}, L > 64,
-                              * a GDN2 log in the WY form */
+                              * a GDN2 log in the WY form, an INT8 base without a
+                              * factor-form log of a delta-rule variant, an eager step
+                              * on an INT8 base */
     DL_ERR_SIZE = 3,         /* caller memory smaller than dl_state_bytes() */
     DL_ERR_LAUNCH = 4,       /* the HIP runtime rejected a launch or copy */
     DL_ERR_STATE = 5         /* dl_state_check found device flags set */
@@ -101,6 +103,25 @@ typedef enum {
 #define DL_FLAG_LOG_FULL   0x1  /* dl_decode_step_log met a full log: row skipped, o = NaN */
 #define DL_FLAG_LOG_NONEMPTY 0x2 /* dl_decode_step_eager met a non-empty log: row skipped, o = NaN */
 #define DL_FLAG_BAD_SLOT   0x4  /* a slot index outside [0, units): row skipped, o = NaN */
+#define DL_FLAG_BAD_KEPT   0x8  /* kept-channel indices not increasing in [0, d_k): row skipped */
+
+/* How the dense base is stored (dl_desc.base_format). */
+typedef enum {
+    DL_BASE_F32 = 0,         /* fp32 [units, H, d_v, d_k] */
+    DL_BASE_I8 = 1           /* mixed precision (a reading of the DAMP abstract, "DAMP:
+                              * Decay-Aware Mixed-Precision Recurrent-State
+                              * Quantization", Jianchao Tan author page: most of the state
+                              * in INT8, a few channels chosen offline kept at higher
+                              * precision): kept_channels key channels per head stay
+                              * fp32; every other entry is a symmetric INT8 code with one
+                              * fp32 scale per value row, scale_i = max |S_ij| / 127 over
+                              * the coded columns, code_ij = clip(rint(S_ij / scale_i),
+                              * -127, 127) (fp32 divisions, ties to even; all codes 0 for
+                              * a zero row), kept columns coded 0.  The base is quantised
+                              * on dl_base_import and at every merge, from the fp32
+                              * merged state; steps read it as code * scale.  Factor-form
+                              * logs of the delta-rule variants only. */
+} dl_base_format;
 
 /* Shape of one state block. */
 typedef struct {
@@ -116,6 +137,8 @@ typedef struct {
                             * the same pass and leaves fill at 0 (that entry
                             * is not written to the log) */
     int32_t log_form;  /* dl_log_form */
+    int32_t base_format;   /* dl_base_format (0: fp32) */
+    int32_t kept_channels; /* DL_BASE_I8: key channels per head kept in fp32, 0 .. 16 */
 } dl_desc;
 
 /* Device pointers into a state block (all row-major, contiguous).
@@ -136,6 +159,14 @@ typedef struct {
  *   fill     [units, H] int32 -- entries in each log; every head of a unit
  *            advances together, one writer per counter
  *   flags    [1] int32 -- DL_FLAG_* bits
+ *   base_codes [units, H, d_v, d_k] int8, base_scale [units, H, d_v] fp32,
+ *   base_kept [units, H, d_v, M] fp32 (M = kept_channels), kept_idx [H, M]
+ *            int32 -- the DL_BASE_I8 base (then `base` is NULL; these are NULL
+ *            for DL_BASE_F32): codes, row scales, the kept channels' values
+ *            and their column indices, strictly increasing in [0, d_k), the
+ *            same for every unit of a head.  dl_state_alloc sets kept_idx to
+ *            evenly spaced channels (m d_k / M + d_k / (2 M)); write other
+ *            indices through this view before the first import or step.
  * log_* are NULL when L == 0. */
 typedef struct {
     float *base;
@@ -146,6 +177,10 @@ typedef struct {
     float *log_t;
     int32_t *fill;
     int32_t *flags;
+    int8_t *base_codes;
+    float *base_scale;
+    float *base_kept;
+    int32_t *kept_idx;
 } dl_state_ptrs;
 
 typedef struct dl_state dl_state;   /* opaque host handle */
@@ -259,6 +294,23 @@ dl_status dl_merge(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t 
  * to replay: the same contraction as dl_merge. */
 dl_status dl_merge_replay(dl_state *st, int32_t rows, const int32_t *slot_idx, int32_t mode,
                           void *stream);
+
+/* Write the bases of the rows' units from fp32 states src [rows, H, d_v, d_k]
+ * (device, 16-byte aligned, read-only): a copy for DL_BASE_F32, the
+ * quantisation described at DL_BASE_I8 otherwise (the dense base of the
+ * DeltaLog page's Core Mechanism, stored as DL_BASE_I8 says).  Logs and
+ * fill counts are left as they are: import into empty logs.  Errors as for
+ * the step calls (DL_ERR_INVALID for NULL or misaligned pointers). */
+dl_status dl_base_import(dl_state *st, int32_t rows, const int32_t *slot_idx, const float *src,
+                         void *stream);
+
+/* The bases of the rows' units as fp32 states dst [rows, H, d_v, d_k]
+ * (device, 16-byte aligned): a copy, or code * scale with the kept channels'
+ * values for DL_BASE_I8.  This is the base alone: after dl_merge with
+ * DL_MERGE_ALL it is the logical state (the DeltaLog page, Core Mechanism:
+ * the merge materialises base + log). */
+dl_status dl_base_export(dl_state *st, int32_t rows, const int32_t *slot_idx, float *dst,
+                         void *stream);
 
 /* Readout without an update: o = S_logical q for each row's unit, from the
  * base and whatever the log holds (for an eager state, o = S q) -- the

@@ -23,21 +23,25 @@ DL_GDN, DL_KDA, DL_RWKV6, DL_GDN2 = 0, 1, 2, 3
 DL_F32, DL_BF16 = 0, 1
 DL_MERGE_FULL, DL_MERGE_ALL = 0, 1
 DL_LOG_WY, DL_LOG_FACTORS = 0, 1
-DL_FLAG_LOG_FULL, DL_FLAG_LOG_NONEMPTY, DL_FLAG_BAD_SLOT = 1, 2, 4
+DL_FLAG_LOG_FULL, DL_FLAG_LOG_NONEMPTY, DL_FLAG_BAD_SLOT, DL_FLAG_BAD_KEPT = 1, 2, 4, 8
+DL_BASE_F32, DL_BASE_I8 = 0, 1
 
 
 class DlDesc(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("units", ctypes.c_int32),
                 ("heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("log_len", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("merge_on_step", ctypes.c_int32), ("log_form", ctypes.c_int32)]
+                ("merge_on_step", ctypes.c_int32), ("log_form", ctypes.c_int32),
+                ("base_format", ctypes.c_int32), ("kept_channels", ctypes.c_int32)]
 
 
 class DlStatePtrs(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("log_k", ctypes.c_void_p),
                 ("log_v", ctypes.c_void_p), ("log_g", ctypes.c_void_p),
                 ("log_beta", ctypes.c_void_p), ("log_t", ctypes.c_void_p), ("fill", ctypes.c_void_p),
-                ("flags", ctypes.c_void_p)]
+                ("flags", ctypes.c_void_p), ("base_codes", ctypes.c_void_p),
+                ("base_scale", ctypes.c_void_p), ("base_kept", ctypes.c_void_p),
+                ("kept_idx", ctypes.c_void_p)]
 
 
 class DlError(RuntimeError):
@@ -60,6 +64,8 @@ _SIGS = {
     "dl_merge": (_I, [_P, _I, _P, _I, _P]),
     "dl_merge_replay": (_I, [_P, _I, _P, _I, _P]),
     "dl_readout": (_I, [_P, _I, _P, _P, _P, _P]),
+    "dl_base_import": (_I, [_P, _I, _P, _P, _P]),
+    "dl_base_export": (_I, [_P, _I, _P, _P, _P]),
     "dl_state_check": (_I, [_P, _P, ctypes.POINTER(_I)]),
     "dl_time_next_launch": (_I, [_P, _P, _P]),
     "dl_last_error": (ctypes.c_char_p, []),
@@ -172,6 +178,14 @@ def dl_readout(handle, rows, slot_idx, q, o, stream) -> None:
     _check(load().dl_readout(handle, rows, slot_idx, q, o, stream))
 
 
+def dl_base_import(handle, rows, slot_idx, src, stream) -> None:
+    _check(load().dl_base_import(handle, rows, slot_idx, src, stream))
+
+
+def dl_base_export(handle, rows, slot_idx, dst, stream) -> None:
+    _check(load().dl_base_export(handle, rows, slot_idx, dst, stream))
+
+
 def dl_time_next_launch(handle, start_event, stop_event) -> None:
     _check(load().dl_time_next_launch(handle, start_event, stop_event))
 
@@ -197,12 +211,16 @@ class DecodeState:
     ``[units, H, L]`` and ``log_t`` ``[units, H, L(L-1)/2]`` (the packed
     key-side factors of the delta-rule variants).  With
     ``log_form=DL_LOG_FACTORS`` (GDN, KDA) ``log_v`` holds the fp32 factors
-    ``a_t`` and there is no ``log_beta`` or ``log_t``.
+    ``a_t`` and there is no ``log_beta`` or ``log_t``.  With
+    ``base_format=DL_BASE_I8`` the base is ``base_codes`` ``[units, H, d, d]``
+    int8, ``base_scale`` ``[units, H, d]``, ``base_kept`` ``[units, H, d, M]``
+    and ``kept_idx`` ``[H, M]`` (``M = kept_channels``), and ``base`` is None:
+    read and write it with :meth:`export_base` and :meth:`import_base`.
     """
 
     def __init__(self, variant: int, units: int, heads: int, d: int, log_len: int,
                  dtype: str = "bf16", device="cuda", stream=None, merge_on_step: bool = False,
-                 log_form: int = DL_LOG_WY):
+                 log_form: int = DL_LOG_WY, base_format: int = DL_BASE_F32, kept_channels: int = 0):
         import torch
 
         self.torch = torch
@@ -212,9 +230,10 @@ class DecodeState:
         self.merge_on_step = bool(merge_on_step)
         self.log_form = int(log_form)
         self.factors = self.log_form == DL_LOG_FACTORS and variant != DL_RWKV6
+        self.base_format, self.kept_channels = int(base_format), int(kept_channels)
         self.desc = DlDesc(variant, units, heads, d, d, log_len,
                            DL_BF16 if dtype == "bf16" else DL_F32, int(self.merge_on_step),
-                           self.log_form)
+                           self.log_form, self.base_format, self.kept_channels)
         nbytes = dl_state_bytes(self.desc)
         if nbytes == 0:
             raise DlError(DL_ERR_INVALID, dl_last_error())
@@ -222,7 +241,15 @@ class DecodeState:
         self.handle = dl_state_alloc(self.desc, self.buf.data_ptr(), nbytes, self._stream(stream))
         p = dl_state_view(self.handle)
         U, H, L = units, heads, log_len
-        self.base = self._view(p.base, torch.float32, (U, H, d, d))
+        M = self.kept_channels
+        if self.base_format == DL_BASE_I8:
+            self.base = None
+            self.base_codes = self._view(p.base_codes, torch.int8, (U, H, d, d))
+            self.base_scale = self._view(p.base_scale, torch.float32, (U, H, d))
+            self.base_kept = self._view(p.base_kept, torch.float32, (U, H, d, M)) if M else None
+            self.kept_idx = self._view(p.kept_idx, torch.int32, (H, M)) if M else None
+        else:
+            self.base = self._view(p.base, torch.float32, (U, H, d, d))
         self.fill = self._view(p.fill, torch.int32, (U, H))
         self.flags = self._view(p.flags, torch.int32, (1,))
         if L > 0:
@@ -323,6 +350,25 @@ class DecodeState:
         sp = self._slots(slot_idx, rows)
         fn = dl_merge_replay if replay else dl_merge
         fn(self.handle, rows, sp, mode, self._stream(stream))
+
+    def import_base(self, src, slot_idx=None, stream=None):
+        """Write the bases of ``src.shape[0]`` units from fp32 states ``[rows, H, d, d]``."""
+        rows = src.shape[0]
+        self._tensor("src", src, self.torch.float32, (rows, self.heads, self.d, self.d))
+        dl_base_import(self.handle, rows, self._slots(slot_idx, rows), src.data_ptr(),
+                       self._stream(stream))
+
+    def export_base(self, rows: int | None = None, slot_idx=None, out=None, stream=None):
+        """The units' bases as fp32 states ``[rows, H, d, d]``."""
+        if rows is None:
+            rows = self.units if slot_idx is None else slot_idx.shape[0]
+        t = self.torch
+        if out is None:
+            out = t.empty((rows, self.heads, self.d, self.d), dtype=t.float32, device=self.buf.device)
+        self._tensor("out", out, t.float32, (rows, self.heads, self.d, self.d))
+        dl_base_export(self.handle, rows, self._slots(slot_idx, rows), out.data_ptr(),
+                       self._stream(stream))
+        return out
 
     def readout(self, q, o=None, slot_idx=None, stream=None):
         rows, sp = self._rows(q, slot_idx)

@@ -40,7 +40,8 @@ dl_status ok() {
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct Layout {
-    size_t off_flags, off_fill, off_base, off_k, off_v, off_g, off_b, off_t, total;
+    size_t off_flags, off_fill, off_base, off_k, off_v, off_g, off_b, off_t;
+    size_t off_codes, off_scale, off_kept, off_kidx, total;
 };
 
 dl_status check_desc(const dl_desc *d) {
@@ -66,6 +67,17 @@ dl_status check_desc(const dl_desc *d) {
         return fail(DL_ERR_UNSUPPORTED, "log_len %d > 64 is not built", d->log_len);
     if (d->variant == DL_GDN2 && d->log_len > 0 && d->log_form != DL_LOG_FACTORS)
         return fail(DL_ERR_UNSUPPORTED, "the gated variant's log is built in the factor form only");
+    if (d->base_format != DL_BASE_F32 && d->base_format != DL_BASE_I8)
+        return fail(DL_ERR_INVALID, "unknown base format %d", d->base_format);
+    if (d->base_format == DL_BASE_F32 && d->kept_channels != 0)
+        return fail(DL_ERR_INVALID, "kept_channels applies to an INT8 base only");
+    if (d->base_format == DL_BASE_I8) {
+        if (d->kept_channels < 0 || d->kept_channels > 16)
+            return fail(DL_ERR_INVALID, "kept_channels must be 0 .. 16, got %d", d->kept_channels);
+        if (d->log_len < 1 || d->log_form != DL_LOG_FACTORS || d->variant == DL_RWKV6)
+            return fail(DL_ERR_UNSUPPORTED,
+                        "an INT8 base is built for factor-form logs of the delta-rule variants");
+    }
     const size_t pairs = (size_t)d->units * (size_t)d->heads;
     if (pairs > (size_t)0x7fffffff)
         return fail(DL_ERR_INVALID, "units * heads too large");
@@ -88,8 +100,18 @@ Layout layout_of(const dl_desc &d) {
     off = align256(off + 256);
     l.off_fill = off;
     off = align256(off + pairs * 4);
+    const bool q8 = d.base_format == DL_BASE_I8;
+    const size_t M = q8 ? d.kept_channels : 0;
     l.off_base = off;
-    off = align256(off + pairs * d.d_v * d.d_k * 4);
+    off = align256(off + (q8 ? 0 : pairs * d.d_v * d.d_k * 4));
+    l.off_codes = off;
+    off = align256(off + (q8 ? pairs * d.d_v * d.d_k : 0));
+    l.off_scale = off;
+    off = align256(off + (q8 ? pairs * d.d_v * 4 : 0));
+    l.off_kept = off;
+    off = align256(off + pairs * d.d_v * M * 4);
+    l.off_kidx = off;
+    off = align256(off + (size_t)d.heads * M * 4);
     l.off_k = off;
     off = align256(off + pairs * L * d.d_k * es);
     l.off_v = off;
@@ -237,12 +259,18 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     // entries; once base and log together are well past the cache (1.5x),
     // streaming the base keeps the log entries, read back by every step,
     // resident instead of letting both thrash.
-    const size_t base_bytes = (size_t)desc->units * desc->heads * desc->d_v * desc->d_k * 4;
-    const size_t log_bytes = l.total - l.off_k;
+    const size_t base_bytes = (l.off_k - l.off_base) + (l.off_kidx - l.off_codes);
+    const size_t log_bytes = l.off_codes - l.off_k;
     p.stream = desc->log_len == 0 ? base_bytes > ((size_t)256 << 20)
                                   : base_bytes + log_bytes > ((size_t)384 << 20);
     p.fill = reinterpret_cast<int *>(m + l.off_fill);
-    p.base = reinterpret_cast<float *>(m + l.off_base);
+    p.q8 = desc->base_format == DL_BASE_I8 ? 1 : 0;
+    p.M = p.q8 ? desc->kept_channels : 0;
+    p.base = p.q8 ? nullptr : reinterpret_cast<float *>(m + l.off_base);
+    p.codes = p.q8 ? reinterpret_cast<int8_t *>(m + l.off_codes) : nullptr;
+    p.scale = p.q8 ? reinterpret_cast<float *>(m + l.off_scale) : nullptr;
+    p.kept = p.q8 ? reinterpret_cast<float *>(m + l.off_kept) : nullptr;
+    p.kidx = p.q8 ? reinterpret_cast<int *>(m + l.off_kidx) : nullptr;
     const bool has_log = desc->log_len > 0;
     p.log_k = has_log ? m + l.off_k : nullptr;
     p.log_v = has_log ? m + l.off_v : nullptr;
@@ -253,8 +281,10 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.log_t = (!p.af && dl::packed_t_len(desc->variant, desc->log_len) > 0)
                   ? reinterpret_cast<float *>(m + l.off_t)
                   : nullptr;
-    const hipError_t e = dl::launch_zero(dev_mem, l.total,
-                                         dl::Launch{static_cast<hipStream_t>(stream), nullptr, nullptr});
+    hipError_t e = dl::launch_zero(dev_mem, l.total,
+                                   dl::Launch{static_cast<hipStream_t>(stream), nullptr, nullptr});
+    if (e == hipSuccess)
+        e = dl::launch_kept_default(p, dl::Launch{static_cast<hipStream_t>(stream), nullptr, nullptr});
     if (e != hipSuccess) {
         delete st;
         return fail(DL_ERR_LAUNCH, "zeroing the state block: %s", hipGetErrorString(e));
@@ -279,6 +309,10 @@ dl_status dl_state_view(const dl_state *st, dl_state_ptrs *out) {
     out->log_t = st->p.log_t;
     out->fill = st->p.fill;
     out->flags = st->p.flags;
+    out->base_codes = st->p.codes;
+    out->base_scale = st->p.scale;
+    out->base_kept = st->p.kept;
+    out->kept_idx = st->p.kidx;
     return ok();
 }
 
@@ -291,6 +325,8 @@ dl_status dl_decode_step_eager_ordered(dl_state *st, int32_t rows, const int32_t
         return s;
     if (row_order && !aligned(row_order, 4))
         return fail(DL_ERR_INVALID, "row_order must be 4-byte aligned");
+    if (st->p.q8)
+        return fail(DL_ERR_UNSUPPORTED, "the eager step is built for an fp32 state only");
     if (rows == 0)
         return ok();
     const dl::Params p = with_rows(st->p, rows, row_order);
@@ -360,6 +396,33 @@ dl_status dl_merge_replay(dl_state *st, int32_t rows, const int32_t *slot_idx, i
     return merge_common(st, rows, slot_idx, mode, stream, false);
 }
 
+static dl_status base_io(dl_state *st, int32_t rows, const int32_t *slot_idx, const void *buf,
+                         void *stream, bool import) {
+    dl_status s = check_rows(st, rows, slot_idx);
+    if (s != DL_OK)
+        return s;
+    if (!buf || !aligned(buf, 16))
+        return fail(DL_ERR_INVALID, "the state buffer must be non-NULL and 16-byte aligned");
+    if (rows == 0)
+        return ok();
+    const dl::Launch ln = launch_of(st, stream);
+    const hipError_t e =
+        import ? dl::launch_base_import(st->p, rows, slot_idx, static_cast<const float *>(buf), ln)
+               : dl::launch_base_export(st->p, rows, slot_idx, static_cast<float *>(const_cast<void *>(buf)),
+                                        ln);
+    return launched(st, e, import ? "base import launch" : "base export launch");
+}
+
+dl_status dl_base_import(dl_state *st, int32_t rows, const int32_t *slot_idx, const float *src,
+                         void *stream) {
+    return base_io(st, rows, slot_idx, src, stream, true);
+}
+
+dl_status dl_base_export(dl_state *st, int32_t rows, const int32_t *slot_idx, float *dst,
+                         void *stream) {
+    return base_io(st, rows, slot_idx, dst, stream, false);
+}
+
 dl_status dl_readout(dl_state *st, int32_t rows, const int32_t *slot_idx, const void *q,
                      float *o, void *stream) {
     dl_status s = check_rows(st, rows, slot_idx);
@@ -397,7 +460,9 @@ dl_status dl_state_check(dl_state *st, void *stream, int32_t *flags_out) {
         e = dl::launch_zero(st->p.flags, 256, dl::Launch{hs, nullptr, nullptr});
         if (e != hipSuccess)
             return fail(DL_ERR_LAUNCH, "clearing device flags: %s", hipGetErrorString(e));
-        return fail(DL_ERR_STATE, "device flags 0x%x (1: log full, 2: eager on non-empty log, 4: bad slot)", h);
+        return fail(DL_ERR_STATE,
+                    "device flags 0x%x (1: log full, 2: eager on non-empty log, 4: bad slot, "
+                    "8: bad kept channels)", h);
     }
     return ok();
 }
@@ -426,7 +491,10 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
         return cs;
     const double es = d.in_dtype == DL_BF16 ? 2.0 : 4.0;
     const double dk = d.d_k, dv = d.d_v;
-    const double St = 4.0 * dv * dk;
+    // the base a step reads and a merge writes: fp32, or INT8 codes, row
+    // scales and the kept channels
+    const double St = d.base_format == DL_BASE_I8 ? dv * dk + 4.0 * dv * (1.0 + d.kept_channels)
+                                                  : 4.0 * dv * dk;
     const bool af = factors_form(d);
     const double gb = d.variant == DL_GDN ? 4.0 : 4.0 * dk;       // decay bytes per entry
     const double bb = d.variant == DL_RWKV6 ? 0.0                 // beta bytes per input

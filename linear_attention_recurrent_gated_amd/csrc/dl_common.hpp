@@ -40,6 +40,13 @@ struct Params {
     // workgroups take them in (a device permutation of 0 .. rows - 1)
     int rows;
     const int *row_order;
+    // DL_BASE_I8 (q8 = 1): INT8 codes, row scales, the M kept key channels'
+    // fp32 values and their column indices (per head); base is NULL
+    int q8, M;
+    int8_t *codes;
+    float *scale;
+    float *kept;
+    int *kidx;
 };
 
 template <int D>
@@ -481,6 +488,82 @@ __device__ __forceinline__ float4 lds_load4(const unsigned char *base, int elem)
 }
 
 // ---------------------------------------------------------------------------
+// INT8 base (DL_BASE_I8).  A value row is held by the 8 lanes of a row group,
+// lane s taking the QW = D / 8 consecutive columns QW s .. QW s + QW - 1, so
+// that a row's codes are one 16-byte (D = 128) or 8-byte (D = 64) load per
+// lane.  Kept key channels are coded 0 and carry their fp32 value apart.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Q8Row {
+    static constexpr int QW = D / 8;           // columns per lane
+    static constexpr int NW = QW / 4;          // 32-bit words of codes per lane
+};
+
+// This lane's codes of one row as floats.
+template <int QW>
+__device__ __forceinline__ void q8_unpack(const uint32_t *w, float *x) {
+#pragma unroll
+    for (int f = 0; f < QW; ++f)
+        x[f] = (float)(int)(int8_t)((w[f >> 2] >> (8 * (f & 3))) & 0xff);
+}
+
+// Maximum over the 8 lanes of a row group; all 8 end with the same value.
+__device__ __forceinline__ float max8(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));
+    x = fmaxf(x, dpp_mov<0x4E>(x));
+    x = fmaxf(x, dpp_mov<0x141>(x));
+    return x;
+}
+
+// Quantise one row held as x[QW] on each lane of its row group: the scale is
+// the maximum |x| over the coded columns (this lane's kept columns are the
+// set bits of kbits) divided by 127, each code rint(x / scale) clipped to
+// +-127, kept columns and zero rows coded 0.  Every operation is an IEEE
+// fp32 operation (correctly rounded divisions, ties-to-even rounding), so an
+// fp32 reference taking the same steps decides the same codes.  Returns the
+// scale; writes the lane's codes to w[QW / 4].
+template <int QW>
+__device__ __forceinline__ float q8_quantize_row(const float *x, uint32_t kbits, uint32_t *w) {
+    float amax = 0.f;
+#pragma unroll
+    for (int f = 0; f < QW; ++f)
+        amax = ((kbits >> f) & 1u) ? amax : fmaxf(amax, fabsf(x[f]));
+    amax = max8(amax);
+    const float scale = amax / 127.0f;
+#pragma unroll
+    for (int i = 0; i < QW / 4; ++i)
+        w[i] = 0u;
+    if (scale > 0.f) {
+#pragma unroll
+        for (int f = 0; f < QW; ++f) {
+            float c = __builtin_rintf(x[f] / scale);
+            c = fminf(fmaxf(c, -127.f), 127.f);
+            const int ci = ((kbits >> f) & 1u) ? 0 : (int)c;
+            w[f >> 2] |= (uint32_t)(ci & 0xff) << (8 * (f & 3));
+        }
+    }
+    return scale;
+}
+
+// The kept channels of head h that fall on lane s's columns, as a bit mask,
+// and whether the index list is valid (strictly increasing in [0, D)).
+template <int D>
+__device__ __forceinline__ uint32_t q8_kept_bits(const Params &P, int h, int s, bool &ok) {
+    constexpr int QW = Q8Row<D>::QW;
+    uint32_t bits = 0u;
+    ok = true;
+    int prev = -1;
+    for (int m = 0; m < P.M; ++m) {
+        const int c = P.kidx[h * P.M + m];
+        ok = ok && c > prev && c < D;
+        prev = c;
+        if (c >= 0 && c < D && c / QW == s)
+            bits |= 1u << (c % QW);
+    }
+    return bits;
+}
+
+// ---------------------------------------------------------------------------
 // host launchers (defined in dl_step.hip / dl_merge.hip).  Every kernel goes
 // through hipExtLaunchKernelGGL so that optional start/stop events are
 // recorded by the dispatch itself.
@@ -511,5 +594,11 @@ hipError_t launch_af_readout(const Params &P, int rows, const int *slot_idx, con
                              float *o, const Launch &ln);
 hipError_t launch_af_merge(const Params &P, int rows, const int *slot_idx, int mode,
                            const Launch &ln);
+// base import / export (dl_base.hip)
+hipError_t launch_base_import(const Params &P, int rows, const int *slot_idx, const float *src,
+                              const Launch &ln);
+hipError_t launch_base_export(const Params &P, int rows, const int *slot_idx, float *dst,
+                              const Launch &ln);
+hipError_t launch_kept_default(const Params &P, const Launch &ln);
 
 }  // namespace dl

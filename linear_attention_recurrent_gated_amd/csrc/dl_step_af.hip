@@ -156,6 +156,130 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
     }
 }
 
+// This lane's codes of one INT8 base row (QW bytes), optionally nontemporal.
+template <int D, bool NT>
+__device__ __forceinline__ void load_codes(const int8_t *p, uint32_t *w) {
+    if constexpr (Q8Row<D>::QW == 16) {
+        uint4 u;
+        if constexpr (NT) {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+            u = make_uint4(t.x, t.y, t.z, t.w);
+        } else {
+            u = *reinterpret_cast<const uint4 *>(p);
+        }
+        w[0] = u.x, w[1] = u.y, w[2] = u.z, w[3] = u.w;
+    } else {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        w[0] = u.x, w[1] = u.y;
+    }
+}
+
+template <int D, bool NT>
+__device__ __forceinline__ void store_codes(int8_t *p, const uint32_t *w) {
+    if constexpr (Q8Row<D>::QW == 16) {
+        if constexpr (NT) {
+            typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+            const u32x4 t = {w[0], w[1], w[2], w[3]};
+            __builtin_nontemporal_store(t, reinterpret_cast<u32x4 *>(p));
+        } else {
+            *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    } else {
+        *reinterpret_cast<uint2 *>(p) = make_uint2(w[0], w[1]);
+    }
+}
+
+// The INT8-base merge of this wave's rows: S' = S0 diag(E_c) + sum_{j < ct}
+// a_j kd_j^T with S0 = code * scale (kept channels: their fp32 values), then
+// each row re-quantised (q8_quantize_row) and written back with its scale
+// and kept values.  Rows go RB at a time (RB QW fp32 registers per lane in
+// flight); the codes are read again here (the step that merges in place has
+// just read them, so they come from the cache) to keep them out of the
+// registers the step's readout holds; kd_j is staged in LDS.
+template <int V, int D, bool NT, int RB>
+__device__ __forceinline__ void af_merge_rows_q8(const Params &P, size_t pair, int h, int ct,
+                                                 const unsigned char *smem, const AfPlan &ap,
+                                                 uint32_t kbits) {
+    using SH = Shape<D>;
+    constexpr int QW = Q8Row<D>::QW;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 3, s = lane & 7;
+    const float *sa = reinterpret_cast<const float *>(smem + ap.off_a);
+    const float *skd = reinterpret_cast<const float *>(smem + ap.off_kd);
+    float ec[QW];
+    if constexpr (V == GDN) {
+        const float e = fast_exp(reinterpret_cast<const float *>(smem + ap.off_s)[0]);
+#pragma unroll
+        for (int f = 0; f < QW; ++f)
+            ec[f] = e;
+    } else {
+        const float *slc = reinterpret_cast<const float *>(smem + ap.off_lc);
+#pragma unroll
+        for (int f = 0; f < QW; ++f)
+            ec[f] = fast_exp(slc[QW * s + f]);
+    }
+#pragma unroll
+    for (int it0 = 0; it0 < SH::ITER; it0 += RB) {
+        float x[RB][QW];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int row = wave * SH::RPW + (it0 + b) * 8 + grp;
+            uint32_t cw[Q8Row<D>::NW];
+            load_codes<D, false>(P.codes + (pair * D + row) * D + QW * s, cw);
+            const float sc = P.scale[pair * D + row];
+            q8_unpack<QW>(cw, x[b]);
+#pragma unroll
+            for (int f = 0; f < QW; ++f)
+                x[b][f] *= sc;
+            for (int m = 0; m < P.M; ++m) {
+                const int c = P.kidx[h * P.M + m];
+                if (c / QW == s) {
+                    const float v = P.kept[(pair * D + row) * P.M + m];
+#pragma unroll
+                    for (int f = 0; f < QW; ++f)
+                        x[b][f] = (f == c % QW) ? v : x[b][f];
+                }
+            }
+#pragma unroll
+            for (int f = 0; f < QW; ++f)
+                x[b][f] *= ec[f];
+        }
+        for (int j = 0; j < ct; ++j) {
+            float kd[QW];
+#pragma unroll
+            for (int f = 0; f < QW; f += 4)
+                f4_to(kd + f, *reinterpret_cast<const float4 *>(skd + j * D + QW * s + f));
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+                const float aj = sa[j * D + wave * SH::RPW + (it0 + b) * 8 + grp];
+#pragma unroll
+                for (int f = 0; f < QW; ++f)
+                    x[b][f] += aj * kd[f];
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+            const int row = wave * SH::RPW + (it0 + b) * 8 + grp;
+            uint32_t w[QW / 4];
+            const float scale = q8_quantize_row<QW>(x[b], kbits, w);
+            store_codes<D, NT>(P.codes + (pair * D + row) * D + QW * s, w);
+            if (s == 0)
+                P.scale[pair * D + row] = scale;
+            for (int m = 0; m < P.M; ++m) {
+                const int c = P.kidx[h * P.M + m];
+                if (c / QW == s) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int f = 0; f < QW; ++f)
+                        v = (f == c % QW) ? x[b][f] : v;
+                    P.kept[(pair * D + row) * P.M + m] = v;
+                }
+            }
+        }
+    }
+}
+
 // One workgroup per (row, head).  APPEND: the step (append + readout);
 // otherwise a readout of base + log.  FUSE: the step that fills the log
 // also merges it (fill back to 0).  With bf16 inputs and logs of up to 32
@@ -163,9 +287,9 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
 // workgroups per CU), except where that spills on the hot path (32 entries
 // with per-key decays and the merge in the step, or with gates), which runs
 // three.
-template <int V, int D, typename T, bool APPEND, int MV, bool NT, bool FUSE>
+template <int V, int D, typename T, bool APPEND, int MV, bool NT, bool FUSE, bool Q8>
 __global__ void __launch_bounds__(256, (MV <= 4 && sizeof(T) == 2)
-                                          ? ((MV == 4 && (V == GDN2 || (V == KDA && FUSE))) ? 3 : 4)
+                                          ? ((MV == 4 && !Q8 && (V == GDN2 || (V == KDA && FUSE))) ? 3 : 4)
                                           : 1)
 af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
@@ -212,7 +336,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     // S0 streams in (q and k in S0's column layout, loaded ahead of it) and
     // scaled by E_n after the barriers.  Only where the registers allow it
     // (bf16 inputs, logs of up to 16 entries).
-    constexpr bool EARLY_DOT = V == GDN && sizeof(T) == 2 && MV <= 2;
+    constexpr bool EARLY_DOT = !Q8 && V == GDN && sizeof(T) == 2 && MV <= 2;
     float4 qs[SH::NCH], ks[SH::NCH];
     if constexpr (EARLY_DOT) {
 #pragma unroll
@@ -222,14 +346,41 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
                 ks[m] = Elem<T>::load4(k + io + col_of(s, m, 0));
         }
     }
-    const float *Sp = P.base + pair * D * D;
-    float4 st[SH::ITER][SH::NCH];
+    // the base rows: fp32 (8 lanes per row, lane s holding the columns
+    // 4 s + 32 m + e), or INT8 codes (lane s holding the QW columns from
+    // QW s), their row scales and, on lanes s and s + 8, the kept channels
+    // m = s, s + 8 with their column indices
+    constexpr int QW = Q8Row<D>::QW;
+    float4 st[Q8 ? 1 : SH::ITER][SH::NCH];
+    uint32_t cw[SH::ITER][Q8Row<D>::NW];
+    float sc[SH::ITER], kv[SH::ITER][2];
+    int kc[2] = {0, 0};
+    if constexpr (Q8) {
 #pragma unroll
-    for (int it = 0; it < SH::ITER; ++it) {
-        const int row = wave * SH::RPW + it * 8 + grp;
+        for (int i = 0; i < 2; ++i) {
+            const int m = s + 8 * i;
+            kc[i] = m < P.M ? P.kidx[h * P.M + m] : 0;
+        }
 #pragma unroll
-        for (int m = 0; m < SH::NCH; ++m)
-            st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
+        for (int it = 0; it < SH::ITER; ++it) {
+            const int row = wave * SH::RPW + it * 8 + grp;
+            load_codes<D, NT>(P.codes + (pair * D + row) * D + QW * s, cw[it]);
+            sc[it] = P.scale[pair * D + row];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int m = s + 8 * i;
+                kv[it][i] = m < P.M ? P.kept[(pair * D + row) * P.M + m] : 0.f;
+            }
+        }
+    } else {
+        const float *Sp = P.base + pair * D * D;
+#pragma unroll
+        for (int it = 0; it < SH::ITER; ++it) {
+            const int row = wave * SH::RPW + it * 8 + grp;
+#pragma unroll
+            for (int m = 0; m < SH::NCH; ++m)
+                st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
+        }
     }
     const int cg = lane % G, ro = lane / G, ch0 = 8 * cg;
     Raw8 qr = {}, kr = {};               // q and k on this lane's channels, as loaded
@@ -240,6 +391,15 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     if (APPEND ? (n >= L || n < 0) : (n > L || n < 0)) {
         reject_row(P, orow, D, DL_FLAG_LOG_FULL);
         return;
+    }
+    uint32_t kbits = 0u;
+    if constexpr (Q8) {
+        bool ok;
+        kbits = q8_kept_bits<D>(P, h, s, ok);
+        if (!ok) {
+            reject_row(P, orow, D, DL_FLAG_BAD_KEPT);
+            return;
+        }
     }
 
     // ---- loads that need n: beta, this lane's logged keys (and decays) of
@@ -438,7 +598,22 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     // ---- per row: x = S0 (E k) + sum u_j a_j, a_n = beta (v - x),
     //      o = S0 (E q) + sum r_j a_j + r_n a_n
     float qt[SH::FPL], kt[SH::FPL];
-    if constexpr (!EARLY_DOT) {
+    float qk[2] = {0.f, 0.f}, kk[2] = {0.f, 0.f};   // INT8 base: E q, E k at the kept channels
+    if constexpr (Q8) {
+        static_assert(QW == SH::FPL, "the INT8 lane layout holds as many columns as the fp32 one");
+#pragma unroll
+        for (int f = 0; f < QW; f += 4) {
+            f4_to(qt + f, *reinterpret_cast<const float4 *>(sqe + QW * s + f));
+            if constexpr (APPEND)
+                f4_to(kt + f, *reinterpret_cast<const float4 *>(ske + QW * s + f));
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            qk[i] = s + 8 * i < P.M ? sqe[kc[i]] : 0.f;
+            if constexpr (APPEND)
+                kk[i] = s + 8 * i < P.M ? ske[kc[i]] : 0.f;
+        }
+    } else if constexpr (!EARLY_DOT) {
 #pragma unroll
         for (int m = 0; m < SH::NCH; ++m) {
             f4_to(qt + 4 * m, *reinterpret_cast<const float4 *>(sqe + col_of(s, m, 0)));
@@ -463,7 +638,24 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     for (int it = 0; it < SH::ITER; ++it) {
         const int row = wave * SH::RPW + it * 8 + grp;
         float ao = 0.f, ax = 0.f;
-        if constexpr (EARLY_DOT) {
+        if constexpr (Q8) {
+            float xc[QW];
+            q8_unpack<QW>(cw[it], xc);
+#pragma unroll
+            for (int f = 0; f < QW; ++f) {
+                ao += xc[f] * qt[f];
+                if constexpr (APPEND)
+                    ax += xc[f] * kt[f];
+            }
+            ao *= sc[it];
+            ax *= sc[it];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                ao += kv[it][i] * qk[i];
+                if constexpr (APPEND)
+                    ax += kv[it][i] * kk[i];
+            }
+        } else if constexpr (EARLY_DOT) {
             ao = e_n * p0[it];
             ax = e_n * x0[it];
         } else {
@@ -523,7 +715,10 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
         if constexpr (FUSE) {
             if (merging) {
                 wave_lds_sync();   // this wave's rows of a_n are in LDS
-                af_merge_rows<V, D, NT>(P, pair, ct, smem, ap, st);
+                if constexpr (Q8)
+                    af_merge_rows_q8<V, D, NT, 1>(P, pair, h, ct, smem, ap, kbits);
+                else
+                    af_merge_rows<V, D, NT>(P, pair, ct, smem, ap, st);
                 if (tid == 0)
                     P.fill[pair] = 0;
                 return;
@@ -536,7 +731,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
 
 // Merge of the selected units' logs into their bases (DL_MERGE_FULL: full
 // logs; DL_MERGE_ALL: every non-empty log).
-template <int V, int D, typename T, bool NT>
+template <int V, int D, typename T, bool NT, bool Q8>
 __global__ void __launch_bounds__(256) af_merge_kernel(Params P, const int *__restrict__ slot_idx,
                                                        int mode) {
     static_assert(V == GDN || V == KDA || V == GDN2, "delta-rule variants only");
@@ -548,16 +743,27 @@ __global__ void __launch_bounds__(256) af_merge_kernel(Params P, const int *__re
         return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 3, s = lane & 7;
+    const int h = (int)(pair % (size_t)P.heads);
     const AfPlan ap = af_plan(D, P.L, true);
     const size_t e0 = pair * P.L;
-    const float *Sp = P.base + pair * D * D;
-    float4 st[SH::ITER][SH::NCH];
+    float4 st[Q8 ? 1 : SH::ITER][SH::NCH];
+    uint32_t kbits = 0u;
+    if constexpr (Q8) {
+        bool ok;
+        kbits = q8_kept_bits<D>(P, h, s, ok);
+        if (!ok) {
+            reject_row(P, nullptr, D, DL_FLAG_BAD_KEPT);
+            return;
+        }
+    } else {
+        const float *Sp = P.base + pair * D * D;
 #pragma unroll
-    for (int it = 0; it < SH::ITER; ++it) {
-        const int row = wave * SH::RPW + it * 8 + grp;
+        for (int it = 0; it < SH::ITER; ++it) {
+            const int row = wave * SH::RPW + it * 8 + grp;
 #pragma unroll
-        for (int m = 0; m < SH::NCH; ++m)
-            st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
+            for (int m = 0; m < SH::NCH; ++m)
+                st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
+        }
     }
     af_stage_factors(P, pair, n, D, smem, ap, lane, wave);
     float *sf = reinterpret_cast<float *>(smem + ap.off_f);
@@ -604,7 +810,10 @@ __global__ void __launch_bounds__(256) af_merge_kernel(Params P, const int *__re
         }
     }
     __syncthreads();
-    af_merge_rows<V, D, NT>(P, pair, n, smem, ap, st);
+    if constexpr (Q8)
+        af_merge_rows_q8<V, D, NT, 2>(P, pair, h, n, smem, ap, kbits);
+    else
+        af_merge_rows<V, D, NT>(P, pair, n, smem, ap, st);
     if (tid == 0)
         P.fill[pair] = 0;
 }
@@ -643,19 +852,24 @@ static void af_launch(const Params &P, int rows, const int *slot_idx, const void
     const bool fuse = APPEND && P.fuse;
     const AfPlan ap = af_plan(D, P.L, fuse);
     const dim3 grid(rows * P.heads), block(256);
-#define DL_AF_LAUNCH(NTV, FV)                                                                          \
-    hipExtLaunchKernelGGL((af_step_kernel<V, D, T, APPEND, MV, NTV, FV>), grid, block, ap.bytes,       \
+#define DL_AF_LAUNCH(NTV, FV, QV)                                                                      \
+    hipExtLaunchKernelGGL((af_step_kernel<V, D, T, APPEND, MV, NTV, FV, QV>), grid, block, ap.bytes,   \
                           ln.stream, ln.start, ln.stop, 0, P, slot_idx, static_cast<const T *>(q),     \
                           static_cast<const T *>(k), static_cast<const T *>(v), g, beta, o)
+#define DL_AF_LAUNCH_Q(NTV, FV)                                                                        \
+    do {                                                                                               \
+        if (P.q8) DL_AF_LAUNCH(NTV, FV, true); else DL_AF_LAUNCH(NTV, FV, false);                      \
+    } while (0)
     if constexpr (APPEND) {
         if (P.stream) {
-            if (fuse) DL_AF_LAUNCH(true, true); else DL_AF_LAUNCH(true, false);
+            if (fuse) DL_AF_LAUNCH_Q(true, true); else DL_AF_LAUNCH_Q(true, false);
         } else {
-            if (fuse) DL_AF_LAUNCH(false, true); else DL_AF_LAUNCH(false, false);
+            if (fuse) DL_AF_LAUNCH_Q(false, true); else DL_AF_LAUNCH_Q(false, false);
         }
     } else {
-        if (P.stream) DL_AF_LAUNCH(true, false); else DL_AF_LAUNCH(false, false);
+        if (P.stream) DL_AF_LAUNCH_Q(true, false); else DL_AF_LAUNCH_Q(false, false);
     }
+#undef DL_AF_LAUNCH_Q
 #undef DL_AF_LAUNCH
 }
 
@@ -690,12 +904,15 @@ template <int V, int D, typename T>
 static hipError_t af_merge_t(const Params &P, int rows, const int *slot_idx, int mode,
                              const Launch &ln) {
     const AfPlan ap = af_plan(D, P.L, true);
-    if (P.stream)
-        hipExtLaunchKernelGGL((af_merge_kernel<V, D, T, true>), dim3(rows * P.heads), dim3(256), ap.bytes,
-                              ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode);
-    else
-        hipExtLaunchKernelGGL((af_merge_kernel<V, D, T, false>), dim3(rows * P.heads), dim3(256), ap.bytes,
-                              ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode);
+#define DL_AFM_LAUNCH(NTV, QV)                                                                         \
+    hipExtLaunchKernelGGL((af_merge_kernel<V, D, T, NTV, QV>), dim3(rows * P.heads), dim3(256), ap.bytes, \
+                          ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode)
+    if (P.stream) {
+        if (P.q8) DL_AFM_LAUNCH(true, true); else DL_AFM_LAUNCH(true, false);
+    } else {
+        if (P.q8) DL_AFM_LAUNCH(false, true); else DL_AFM_LAUNCH(false, false);
+    }
+#undef DL_AFM_LAUNCH
     return hipGetLastError();
 }
 

@@ -64,6 +64,28 @@ def test_state_bytes(variant, d, L, dt, es, form):
     assert B.dl_state_bytes(desc) == _expected_bytes(variant, 7, 3, d, L, es, form)
 
 
+@pytest.mark.parametrize("variant", [B.DL_GDN, B.DL_KDA, B.DL_GDN2])
+@pytest.mark.parametrize("d,L,M", [(128, 32, 8), (64, 16, 0), (128, 1, 16)])
+def test_state_bytes_int8_base(variant, d, L, M):
+    """INT8 base: codes, row scales, kept values and indices replace the fp32 base."""
+    U, H = 7, 3
+    desc = B.DlDesc(variant, U, H, d, d, L, B.DL_BF16, 0, B.DL_LOG_FACTORS, B.DL_BASE_I8, M)
+    fp32 = _expected_bytes(variant, U, H, d, L, 2, B.DL_LOG_FACTORS)
+    pairs = U * H
+    q8 = _align(pairs * d * d) + _align(pairs * d * 4) + _align(pairs * d * M * 4) + _align(H * M * 4)
+    assert B.dl_state_bytes(desc) == fp32 - _align(pairs * d * d * 4) + q8
+
+
+def test_suggest_log_len_int8_base_models_the_smaller_base():
+    """With a base a quarter the size, a step's base read weighs less, so the
+    traffic model's best log is no longer (it amortises less) and costs less."""
+    f = B.DlDesc(B.DL_GDN, 1, 1, 128, 128, 0, B.DL_BF16, 1, B.DL_LOG_FACTORS)
+    q = B.DlDesc(B.DL_GDN, 1, 1, 128, 128, 0, B.DL_BF16, 1, B.DL_LOG_FACTORS, B.DL_BASE_I8, 8)
+    Lf, bf = B.dl_suggest_log_len(f)
+    Lq, bq = B.dl_suggest_log_len(q)
+    assert bq < 0.5 * bf and Lq <= Lf
+
+
 def test_state_bytes_full_size_configs():
     # 64 x 32 heads of 128 x 128 fp32 = 128 MiB of state plus the log
     desc = B.DlDesc(B.DL_GDN, 64, 32, 128, 128, 16, B.DL_BF16)
@@ -84,6 +106,12 @@ def test_state_bytes_full_size_configs():
     ((0, 4, 2, 128, 128, 8, B.DL_BF16, 0, 2), B.DL_ERR_INVALID),  # unknown log form
     ((4, 4, 2, 128, 128, 8, B.DL_BF16), B.DL_ERR_INVALID),        # unknown variant
     ((3, 4, 2, 128, 128, 8, B.DL_BF16, 0, 0), B.DL_ERR_UNSUPPORTED),  # gated log in WY form
+    ((0, 4, 2, 128, 128, 8, B.DL_BF16, 0, 1, 2), B.DL_ERR_INVALID),   # unknown base format
+    ((0, 4, 2, 128, 128, 8, B.DL_BF16, 0, 1, 0, 4), B.DL_ERR_INVALID),  # kept channels, fp32 base
+    ((0, 4, 2, 128, 128, 8, B.DL_BF16, 0, 1, 1, 17), B.DL_ERR_INVALID),  # too many kept channels
+    ((0, 4, 2, 128, 128, 8, B.DL_BF16, 0, 0, 1, 4), B.DL_ERR_UNSUPPORTED),  # INT8 base, WY log
+    ((2, 4, 2, 64, 64, 8, B.DL_BF16, 0, 1, 1, 4), B.DL_ERR_UNSUPPORTED),  # INT8 base, RWKV6
+    ((0, 4, 2, 128, 128, 0, B.DL_BF16, 0, 1, 1, 4), B.DL_ERR_UNSUPPORTED),  # INT8 base, no log
 ])
 def test_bad_descriptors(lib, fields, code):
     desc = B.DlDesc(*fields)
@@ -117,6 +145,8 @@ def test_null_handle_is_rejected(lib):
     assert lib.dl_merge(None, 1, None, 0, None) == B.DL_ERR_INVALID
     assert lib.dl_merge_replay(None, 1, None, 0, None) == B.DL_ERR_INVALID
     assert lib.dl_readout(None, 1, None, p, p, None) == B.DL_ERR_INVALID
+    assert lib.dl_base_import(None, 1, None, p, None) == B.DL_ERR_INVALID
+    assert lib.dl_base_export(None, 1, None, p, None) == B.DL_ERR_INVALID
     assert lib.dl_state_check(None, None, None) == B.DL_ERR_INVALID
     assert lib.dl_state_view(None, None) == B.DL_ERR_INVALID
     assert lib.dl_state_free(None) == B.DL_OK

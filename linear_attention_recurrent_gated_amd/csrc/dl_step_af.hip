@@ -289,7 +289,7 @@ __device__ __forceinline__ void af_merge_rows_q8(const Params &P, size_t pair, i
 // three.
 template <int V, int D, typename T, bool APPEND, int MV, bool NT, bool FUSE, bool Q8>
 __global__ void __launch_bounds__(256, (MV <= 4 && sizeof(T) == 2)
-                                          ? ((MV == 4 && !Q8 && (V == GDN2 || (V == KDA && FUSE))) ? 3 : 4)
+                                          ? (Q8 ? 4 : ((MV == 4 && (V == GDN2 || (V == KDA && FUSE))) ? 3 : 4))
                                           : 1)
 af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,

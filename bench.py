@@ -7,6 +7,12 @@ read-only base (dl_decode_step_log) and merges full logs into the base --
 with a separate launch (dl_merge) or inside the step that fills them
 (merge_on_step) -- keeping either the compact-WY log or the additive-factor
 log (log_form); the eager path rewrites every state (dl_decode_step_eager).
+With several layers, a path with separate merges keeps every layer's states
+in one state block (layer l's sequences at slots l B .. l B + B - 1) and
+launches one merge per token, after the last layer's step, over the full
+logs of every layer: a layer's merge still lands after its step and before
+its next one, and the launch fills the GPU where a per-layer one (about
+B / L sequences) would not.
 Inputs for all steps are resident in HBM before timing starts.  One JSON
 line is printed:
 
@@ -258,6 +264,12 @@ def parse_args(argv=None):
                          "paths, never as the headline)")
     ap.add_argument("--order", default="auto", choices=ORDERS,
                     help="dispatch order of the rows of steps that merge in place (ragged logs)")
+    ap.add_argument("--merge-schedule", default="auto", choices=("auto", "layer", "token"),
+                    help="separate merges: 'layer' launches one after each layer's step (one "
+                         "state block per layer); 'token' keeps every layer's states in one "
+                         "block and launches one merge per token, after the last layer's step, "
+                         "over every layer's full logs; 'auto' is 'token' when the workload has "
+                         "several layers")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target wall time of the oracle sample")
@@ -328,6 +340,7 @@ def main(argv=None):
     prefix = wl.prefix_steps(L)
     T = prefix + Wu + K
     H, d, Bt, layers = wl.heads, wl.d_k, wl.batch, wl.layers
+    token_merges = args.merge_schedule == "token" or (args.merge_schedule == "auto" and layers > 1)
     U = wl.units_total
     P = U * H
     paths = args.paths.split(",")
@@ -420,18 +433,26 @@ def main(argv=None):
         q8 = path.endswith("-i8")
         fused = "-fused" in path
         separate = path in ("log", "af", "af-i8")     # merges launched after the step
+        # one state block per layer, or (merges per token) one block holding
+        # every layer's states, layer l's units at l Bt .. l Bt + Bt - 1
+        pooled = separate and token_merges and layers > 1
+        nblk, ublk = (1, layers * Bt) if pooled else (layers, Bt)
         states = []
-        for l in range(layers):
-            st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype, device=dev,
+        for l in range(nblk):
+            st = B.DecodeState(wl.variant, ublk, H, d, 0 if path == "eager" else L, wl.dtype, device=dev,
                                merge_on_step=fused,
                                log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY,
                                base_format=B.DL_BASE_I8 if q8 else B.DL_BASE_F32,
                                kept_channels=KEPT_CHANNELS if q8 else 0)
             if q8:
-                st.import_base(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]).to(dev))
+                st.import_base(torch.from_numpy(S0[l * ublk:(l + 1) * ublk]).to(dev))
             else:
-                st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
+                st.base.copy_(torch.from_numpy(S0[l * ublk:(l + 1) * ublk]))
             states.append(st)
+        layer_state = [states[0] if pooled else states[l] for l in range(layers)]
+        # pooled: layer l's steps name its units by slot (l Bt + batch index)
+        layer_slots = [torch.arange(l * Bt, (l + 1) * Bt, dtype=torch.int32, device=dev)
+                       for l in range(layers)] if pooled else None
         kept_idx = states[0].kept_idx.cpu().numpy() if q8 else None
         O = torch.zeros((T, U, H, d), dtype=torch.float32, device=dev)
         stream = torch.cuda.current_stream().cuda_stream
@@ -460,15 +481,20 @@ def main(argv=None):
                     order_p = order_t.data_ptr()
             merge_slots = None
             if wl.ragged and separate and len(full_next):
-                merge_slots = torch.from_numpy(full_next.astype(np.int32)).to(dev)
+                # the full units of one layer, or (pooled) of every layer
+                ms = np.concatenate([l * Bt + full_next for l in range(layers)]) if pooled else full_next
+                merge_slots = torch.from_numpy(ms.astype(np.int32)).to(dev)
                 keep.append(merge_slots)
             for l in range(layers):
-                st = states[l]
+                st = layer_state[l]
                 lo, hi = l * Bt, (l + 1) * Bt
                 if len(act[tau]) == 0:
                     continue
                 if tau in gathers:
                     idx, slot, rows = gathers[tau]
+                    if pooled:
+                        slot = slot + l * Bt
+                        keep.append(slot)
                     xs = [x[tau, lo:hi].index_select(0, idx).contiguous() for x in (Q, Kt, V, G)]
                     xs.append(Bb[tau, lo:hi].index_select(0, idx).contiguous() if Bb is not None else None)
                     o = torch.empty((rows, H, d), dtype=torch.float32, device=dev)
@@ -477,17 +503,19 @@ def main(argv=None):
                 else:
                     xs = [Q[tau, lo:hi], Kt[tau, lo:hi], V[tau, lo:hi], G[tau, lo:hi],
                           None if Bb is None else Bb[tau, lo:hi]]
-                    rows, sp, op, o = Bt, None, order_p, O[tau, lo:hi]
+                    rows, op, o = Bt, order_p, O[tau, lo:hi]
+                    sp = layer_slots[l].data_ptr() if pooled else None
                 ptrs = [None if x is None else x.data_ptr() for x in xs]
                 plan.append((tau, "step", st.handle, (rows, sp, op, *ptrs, o.data_ptr(), stream)))
                 if path != "eager":
                     if l == 0:
                         fills[act[tau]] += 1
-                    if separate and merge_slots is not None:
-                        plan.append((tau, "merge", st.handle,
-                                     (len(full_next), merge_slots.data_ptr(), B.DL_MERGE_FULL, stream)))
-                    elif separate and np.any(fills == L):
-                        plan.append((tau, "merge", st.handle, (Bt, None, B.DL_MERGE_FULL, stream)))
+                    if separate and (not pooled or l == layers - 1):
+                        if merge_slots is not None:
+                            plan.append((tau, "merge", st.handle, (len(merge_slots), merge_slots.data_ptr(),
+                                                                   B.DL_MERGE_FULL, stream)))
+                        elif np.any(fills == L):
+                            plan.append((tau, "merge", st.handle, (st.units, None, B.DL_MERGE_FULL, stream)))
                     if l == layers - 1:
                         fills[fills == L] = 0
         timed = [(kind, h, a) for tau, kind, h, a in plan if tau >= t_first]
@@ -535,7 +563,7 @@ def main(argv=None):
         ev.close()
         if path != "eager":
             for st in states:
-                B.dl_merge(st.handle, Bt, None, B.DL_MERGE_ALL, stream)
+                B.dl_merge(st.handle, st.units, None, B.DL_MERGE_ALL, stream)
         flags = [st.check() for st in states]
         assert not any(flags), f"device flags {flags}"
         # algorithmic bytes of the timed launches: the path's own byte model
@@ -619,7 +647,8 @@ def main(argv=None):
                      "batch": Bt, "layers": layers, "heads": H, "d_k": d, "d_v": wl.d_v,
                      "log_len": L, "input_dtype": wl.dtype, "state_dtype": "fp32",
                      "ragged_offsets": wl.ragged, "untimed_prefix_steps": prefix,
-                     "row_order": args.order}
+                     "row_order": args.order,
+                     "merge_schedule": "token" if token_merges and layers > 1 else "layer"}
     if args.warmup is not None and Wu != args.warmup:
         out["warmup_requested"] = args.warmup
     # merges inside the timed window: steps at which some log fills, and the

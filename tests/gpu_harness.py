@@ -56,7 +56,10 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
     ``bench_schedule``: launch what the benchmark launches for ragged logs --
     separate merges name only the units whose logs are full (``slot_idx``),
     and a step that merges in place takes its rows in the benchmark's order
-    (``row_order``) -- instead of a merge over every unit after each step.
+    (``row_order``) -- instead of a merge over every unit after each step;
+    with several layers, a path with separate merges keeps every layer's
+    states in one block and merges once per step, after the last layer, over
+    every layer's full logs, as the benchmark does.
     """
     H, d, Bt, layers = wl.heads, wl.d_k, wl.batch, wl.layers
     T = wl.total_steps(L) if steps is None else steps
@@ -70,16 +73,20 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
     fills = np.zeros(Bt, dtype=np.int64)                         # host model of the schedule
 
     S0 = W.initial_state(wl, seed)                               # [U, H, d, d]
-    states = {}
+    def pooled(path):
+        return bench_schedule and wl.ragged and layers > 1 and path in ("log", "log-replay", "af")
+
+    sblocks, states = {}, {}
     for path in paths:
-        per_layer = []
-        for l in range(layers):
-            st = B.DecodeState(wl.variant, Bt, H, d, 0 if path == "eager" else L, wl.dtype,
+        nblk, ublk = (1, layers * Bt) if pooled(path) else (layers, Bt)
+        sblocks[path] = []
+        for l in range(nblk):
+            st = B.DecodeState(wl.variant, ublk, H, d, 0 if path == "eager" else L, wl.dtype,
                                merge_on_step=path.endswith("-fused"),
                                log_form=B.DL_LOG_FACTORS if path.startswith("af") else B.DL_LOG_WY)
-            st.base.copy_(torch.from_numpy(S0[l * Bt:(l + 1) * Bt]))
-            per_layer.append(st)
-        states[path] = per_layer
+            st.base.copy_(torch.from_numpy(S0[l * ublk:(l + 1) * ublk]))
+            sblocks[path].append(st)
+        states[path] = [sblocks[path][0 if pooled(path) else l] for l in range(layers)]
     torch.cuda.synchronize()
 
     rec = {path: [] for path in paths}
@@ -139,12 +146,18 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
                         slot = torch.from_numpy(act.astype(np.int32)).cuda()
                         args = tuple(None if x is None else x[lo:hi].index_select(0, idx).contiguous()
                                      for x in (q, k, v, g, beta))
+                    if pooled(path):                  # layer l's units in the shared block
+                        slot = torch.from_numpy((l * Bt + act).astype(np.int32)).cuda()
                     if path == "eager":
                         o = st.step_eager(*args, slot_idx=slot)
                     else:
                         o = st.step_log(*args, slot_idx=slot, row_order=order)
                         if bench_schedule and wl.ragged:
-                            if not path.endswith("-fused") and len(full_next):
+                            if pooled(path) and len(full_next) and l == layers - 1:
+                                ms = np.concatenate([j * Bt + full_next for j in range(layers)])
+                                st.merge(B.DL_MERGE_FULL, slot_idx=torch.from_numpy(ms.astype(np.int32)).cuda(),
+                                         replay=(path == "log-replay"))
+                            elif not pooled(path) and not path.endswith("-fused") and len(full_next):
                                 st.merge(B.DL_MERGE_FULL, slot_idx=torch.from_numpy(
                                     full_next.astype(np.int32)).cuda(), replay=(path == "log-replay"))
                         elif merge_every_step or (tau + 1) % L == 0:
@@ -165,18 +178,17 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
     case = Case()
     for path in paths:
         finals = []
-        for l in range(layers):
-            st = states[path][l]
+        for st in sblocks[path]:
             if path != "eager":
                 st.merge(B.DL_MERGE_ALL, replay=(path == "log-replay"))
             finals.append(st.base)
-        flags = [st.check() for st in states[path]]
+        flags = [st.check() for st in sblocks[path]]
         assert not any(flags), f"device flags {flags} on path {path}"
         Sfull = torch.cat(finals, 0)                              # [U, H, d, d]
         S_sel = Sfull[sel_u_t, sel_h_t].double().cpu().numpy()
         o_sel = torch.stack(rec[path], 1).double().cpu().numpy()  # [n_sel, T, d]
         case.gpu[path] = (o_sel, S_sel)
-        for st in states[path]:
+        for st in sblocks[path]:
             st.close()
     if run_oracle:
         beta_arr = np.stack(b_sel) if b_sel else None

@@ -24,6 +24,10 @@ line is printed:
                  duration, against 8 TB/s; the path's own byte model beside
                  it; the counter-measured bytes per launch ("traffic") when
                  the committed profile matches the sources
+  roofline.ceiling
+                 what a plain streaming kernel (dl_stream_probe: 16-byte
+                 nontemporal loads, nothing else) reaches on this machine, read
+                 and copy, and the step kernel's rate as a share of the read
   write_traffic_reduction
                  dense-state write bytes of eager over DeltaLog (model, and
                  from the committed counters when they match the sources)
@@ -275,9 +279,45 @@ def parse_args(argv=None):
                     help="target wall time of the oracle sample")
     ap.add_argument("--library", default=None, metavar="PATH",
                     help="load this build of libdeltalog.so instead of the package's")
+    ap.add_argument("--ceiling-mib", type=int, default=4096, metavar="MiB",
+                    help="size of the streaming-rate probe (dl_stream_probe) read after the "
+                         "paths: a plain read of this many MiB and a copy of a quarter of it, "
+                         "the practical ceilings reported beside the published peak (0: skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MiB",
                     help="also run a plain device copy of this size (counter calibration)")
     return ap.parse_args(argv)
+
+
+def stream_ceilings(mib: int, dev, reps: int = 10) -> dict:
+    """Kernel-timed rates of dl_stream_probe: a read of ``mib`` MiB and a copy
+    of a quarter of it (bytes moved per second, median of ``reps``)."""
+    import torch
+
+    from linear_attention_recurrent_gated_amd import binding as B
+
+    nbytes = mib * 2**20
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    out = torch.empty(nbytes // 32768 + 1, dtype=torch.float32, device=dev)
+    cb = nbytes // 4
+    dst = torch.empty(cb // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents()
+    res = {}
+    for mode, name, moved, dptr, n in ((B.DL_PROBE_READ, "read", nbytes, out.data_ptr(), nbytes),
+                                       (B.DL_PROBE_COPY, "copy", 2 * cb, dst.data_ptr(), cb)):
+        B.dl_stream_probe(mode, src.data_ptr(), dptr, n, stream)
+        pairs = [ev.pair() for _ in range(reps)]
+        for a, b in pairs:
+            B.dl_stream_probe(mode, src.data_ptr(), dptr, n, stream, a, b)
+        torch.cuda.synchronize()
+        ms = float(np.median([ev.ms(a, b) for a, b in pairs]))
+        res[f"{name}_GBps"] = moved / (ms / 1e3) / 1e9
+        res[f"{name}_bytes"] = moved
+    ev.close()
+    del src, out, dst
+    torch.cuda.empty_cache()
+    res["kernel"] = "dl_stream_probe"
+    return res
 
 
 class HipEvents:
@@ -631,6 +671,11 @@ def main(argv=None):
             f"({res['method_GBps']:.0f} GB/s method bytes, {res['step_kernel_GBps']:.0f} GB/s "
             f"path bytes), merges {len(merge_ms)} ({res['merge_ms_total']:.3f} ms)")
 
+    ceiling = None
+    if args.ceiling_mib > 0:
+        ceiling = stream_ceilings(args.ceiling_mib, dev)
+        log(f"[bench] streaming probe: read {ceiling['read_GBps']:.0f} GB/s, "
+            f"copy {ceiling['copy_GBps']:.0f} GB/s")
     if args.copy_probe:
         n = args.copy_probe * 2**20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -687,6 +732,10 @@ def main(argv=None):
                                "frac": res["step_kernel_GBps"] / HBM_PEAK_GBPS}}
 
     out["roofline"] = roof(r, kname, L if main_path in knames else None)
+    if ceiling is not None:
+        # what a plain kernel reaches on this memory system, beside the peak
+        out["roofline"]["ceiling"] = dict(ceiling, frac_of_read=out["roofline"]["achieved"]
+                                          / ceiling["read_GBps"])
     if "eager" in results and main_path != "eager":
         e = results["eager"]
         out["eager"] = {"value": e["updates_per_s"], "ms_per_step": e["ms_per_step"],
@@ -717,6 +766,10 @@ def main(argv=None):
                            "fp32_peak_frac": (u["merge_flops"] / ms / 1e12 / FP32_MFMA_PEAK_TFLOPS)
                            if ms else None}
     if merges:
+        if ceiling is not None:
+            for mg in merges.values():
+                if mg["GBps"]:
+                    mg["frac_of_copy"] = mg["GBps"] / ceiling["copy_GBps"]
         out["merge"] = merges
     # the INT8-base paths: a quantised state, so never the headline; reported
     # beside it with their own byte model
@@ -781,9 +834,14 @@ def main(argv=None):
             parity[path] = {"max_rel_err_outputs": float(eo), "max_rel_err_state": float(es),
                             "ok": bool(eo <= 2e-4 and es <= 2e-4)}
         # INT8-base paths against the oracle's quantised-base recurrence (the
-        # base re-quantised at every merge), on the first 32 sampled states:
-        # informational, since a code that an fp32 state takes on the other
-        # side of a rounding boundary shifts that entry by one INT8 step
+        # base re-quantised at every merge), on the first 32 sampled states.
+        # The import quantises the same fp32 states on both sides (the same
+        # codes), so every output up to a state's first merge must match to
+        # the tolerance; after a merge each side quantises its own fp32 /
+        # float64 state, and an entry within rounding distance of a code
+        # boundary may take the neighbouring code (one INT8 step), so later
+        # outputs and the final state are reported, not judged (the GPU tests
+        # check the merges' codes entry by entry, re-synchronising at each).
         from oracle import quant
         for path, res in results.items():
             if not path.endswith("-i8"):
@@ -796,13 +854,17 @@ def main(argv=None):
                 S0.reshape(P, d, d)[sample[:n]], t_start[:n], L, kept, threads=1)
             o = res["o_sample"][:, :n]
             scale_o = np.maximum(1.0, np.abs(o_q).max(axis=(0, 2)))
-            eo = (np.abs(o - o_q).max(axis=(0, 2)) / scale_o).max()
+            err = np.abs(o - o_q).max(axis=2) / scale_o                 # [T, n]
+            first = np.arange(T)[:, None] < (t_start[:n] + L)[None, :]   # up to the first merge
+            e_first = float(np.where(first, err, 0.0).max())
             S_q = quant.dequantize_base(*fin, kept)
             scale_s = np.maximum(1.0, np.abs(S_q).reshape(n, -1).max(axis=1))
             es = (np.abs(res["S_sample"][:n] - S_q).reshape(n, -1).max(axis=1) / scale_s).max()
-            parity[path] = {"max_rel_err_outputs": float(eo), "max_rel_err_state": float(es),
+            parity[path] = {"max_rel_err_outputs_to_first_merge": e_first,
+                            "max_rel_err_outputs_all_steps": float(err.max()),
+                            "max_rel_err_state": float(es),
                             "reference": "oracle.quant.run_quantized_base", "states": n,
-                            "ok": bool(eo <= 2e-4)}
+                            "ok": bool(e_first <= 2e-4)}
         out["parity"] = parity
     print(json.dumps(out), flush=True)
     return 0

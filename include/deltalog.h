@@ -361,6 +361,25 @@ int32_t dl_version(void);
  * for the descriptor with log_len = 1, or a NULL L_out. */
 dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_out);
 
+/* Streaming-rate calibration, not part of the method: one launch that only
+ * moves bytes, in the access pattern of the state kernels' largest stream
+ * (16-byte nontemporal loads, 256 threads per workgroup), so that a kernel's
+ * achieved rate can be set beside what a plain kernel reaches on this memory
+ * system as well as beside the published peak.
+ *   DL_PROBE_READ: reads `bytes` of `src` and writes, per 32 KiB of it, the
+ *     float32 sum of that block's float32 values to `dst` (dst holds
+ *     ceil(bytes / 32768) floats);
+ *   DL_PROBE_COPY: copies `bytes` of `src` to `dst` (non-overlapping).
+ * src and dst are device pointers (caller-owned, 16-byte aligned); bytes is
+ * a positive multiple of 16.  `start_event` / `stop_event`, if given (both or
+ * neither), are recorded at the kernel's own dispatch begin and end, as
+ * dl_time_next_launch arms them.  Asynchronous on `stream`.  Errors:
+ * DL_ERR_INVALID (mode, NULL or misaligned pointer, bytes, one event),
+ * DL_ERR_UNSUPPORTED (more than 2^31 - 1 blocks of 32 KiB), DL_ERR_LAUNCH. */
+typedef enum { DL_PROBE_READ = 0, DL_PROBE_COPY = 1 } dl_probe_mode;
+dl_status dl_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes, void *stream,
+                          void *start_event, void *stop_event);
+
 #ifdef __cplusplus
 }
 #endif

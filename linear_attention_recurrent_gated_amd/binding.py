@@ -25,6 +25,7 @@ DL_MERGE_FULL, DL_MERGE_ALL = 0, 1
 DL_LOG_WY, DL_LOG_FACTORS = 0, 1
 DL_FLAG_LOG_FULL, DL_FLAG_LOG_NONEMPTY, DL_FLAG_BAD_SLOT, DL_FLAG_BAD_KEPT = 1, 2, 4, 8
 DL_BASE_F32, DL_BASE_I8 = 0, 1
+DL_PROBE_READ, DL_PROBE_COPY = 0, 1
 
 
 class DlDesc(ctypes.Structure):
@@ -72,6 +73,7 @@ _SIGS = {
     "dl_version": (_I, []),
     "dl_suggest_log_len": (_I, [ctypes.POINTER(DlDesc), ctypes.POINTER(ctypes.c_int32),
                                 ctypes.POINTER(ctypes.c_double)]),
+    "dl_stream_probe": (_I, [_I, _P, _P, ctypes.c_size_t, _P, _P, _P]),
 }
 
 _lib = None
@@ -188,6 +190,10 @@ def dl_base_export(handle, rows, slot_idx, dst, stream) -> None:
 
 def dl_time_next_launch(handle, start_event, stop_event) -> None:
     _check(load().dl_time_next_launch(handle, start_event, stop_event))
+
+
+def dl_stream_probe(mode, src, dst, nbytes, stream, start_event=None, stop_event=None) -> None:
+    _check(load().dl_stream_probe(mode, src, dst, nbytes, stream, start_event, stop_event))
 
 
 def dl_state_check(handle, stream) -> int:

@@ -530,4 +530,26 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
     return ok();
 }
 
+dl_status dl_stream_probe(int32_t mode, const void *src, void *dst, size_t bytes, void *stream,
+                          void *start_event, void *stop_event) {
+    if (mode != DL_PROBE_READ && mode != DL_PROBE_COPY)
+        return fail(DL_ERR_INVALID, "unknown probe mode %d", mode);
+    if (!src || !dst)
+        return fail(DL_ERR_INVALID, "src and dst must be non-NULL");
+    if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15)
+        return fail(DL_ERR_INVALID, "src and dst must be 16-byte aligned");
+    if (bytes == 0 || bytes % 16 != 0)
+        return fail(DL_ERR_INVALID, "bytes must be a positive multiple of 16, got %zu", bytes);
+    if (dl::probe_read_outputs(bytes) > 0x7fffffffu)
+        return fail(DL_ERR_UNSUPPORTED, "buffer of %zu bytes is too large for one launch", bytes);
+    if ((start_event == nullptr) != (stop_event == nullptr))
+        return fail(DL_ERR_INVALID, "give both events or neither");
+    const dl::Launch ln{static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(start_event),
+                        static_cast<hipEvent_t>(stop_event)};
+    const hipError_t e = dl::launch_stream_probe(mode, src, dst, bytes, ln);
+    if (e != hipSuccess)
+        return fail(DL_ERR_LAUNCH, "stream probe launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

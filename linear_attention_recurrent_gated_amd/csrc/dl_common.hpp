@@ -600,5 +600,8 @@ hipError_t launch_base_import(const Params &P, int rows, const int *slot_idx, co
 hipError_t launch_base_export(const Params &P, int rows, const int *slot_idx, float *dst,
                               const Launch &ln);
 hipError_t launch_kept_default(const Params &P, const Launch &ln);
+// streaming-rate calibration (dl_probe.hip): mode 0 reads, mode 1 copies
+size_t probe_read_outputs(size_t bytes);
+hipError_t launch_stream_probe(int mode, const void *src, void *dst, size_t bytes, const Launch &ln);
 
 }  // namespace dl

@@ -225,3 +225,24 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         B.load(str(tmp_path / "libdeltalog.so"))
+
+
+def test_stream_probe_rejects_bad_arguments():
+    """Argument checks of the streaming-rate probe, all before any launch."""
+    buf = 4096   # a host address: never dereferenced, every call below is rejected first
+    bad = [
+        (7, buf, buf, 1024, B.DL_ERR_INVALID),                   # unknown mode
+        (B.DL_PROBE_READ, None, buf, 1024, B.DL_ERR_INVALID),    # NULL source
+        (B.DL_PROBE_COPY, buf, None, 1024, B.DL_ERR_INVALID),    # NULL destination
+        (B.DL_PROBE_COPY, buf + 4, buf, 1024, B.DL_ERR_INVALID), # misaligned
+        (B.DL_PROBE_READ, buf, buf, 0, B.DL_ERR_INVALID),        # empty
+        (B.DL_PROBE_READ, buf, buf, 1000, B.DL_ERR_INVALID),     # not a multiple of 16
+        (B.DL_PROBE_READ, buf, buf, 1 << 62, B.DL_ERR_UNSUPPORTED),
+    ]
+    for mode, src, dst, n, want in bad:
+        with pytest.raises(B.DlError) as e:
+            B.dl_stream_probe(mode, src, dst, n, None)
+        assert e.value.status == want, (mode, src, dst, n)
+    with pytest.raises(B.DlError) as e:
+        B.dl_stream_probe(B.DL_PROBE_READ, buf, buf, 1024, None, start_event=buf)
+    assert e.value.status == B.DL_ERR_INVALID

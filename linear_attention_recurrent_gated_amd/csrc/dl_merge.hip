@@ -496,23 +496,33 @@ static void wy_launch(const Params &P, int pairs, const int *slot_idx, int mode,
                               ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode, pairs);
 }
 
-// One workgroup per pair, holding the pair's whole base, while the chunks'
-// z tiles fit beside it in registers (logs of up to 32 entries at d = 128);
-// longer logs split a pair's rows over two workgroups.  (Splitting further,
-// to spread launches over few pairs across more CUs, measured slower: a
-// workgroup's time is set by its chain of loads, barriers and contractions,
-// not by its share of the base.)
+// d = 128: with per-key decays, one workgroup per pair, holding the pair's
+// whole base, while the chunks' z tiles fit beside it in registers (logs of
+// up to 32 entries); with head-wise decay, and for longer logs, a pair's rows
+// split over two workgroups of half the registers (twice the workgroups per
+// CU, each staging the pair's key side again: about 4% faster for GDN at 16
+// and 32 entries, 20% slower for per-key decays at 32, whose key side is
+// twice as large).  Splitting further (four workgroups of two waves) measured
+// slower everywhere: a workgroup's time is set by its chain of loads,
+// barriers and contractions, not by its share of the base.
 template <int V, int D, typename T>
 static hipError_t wy_t(const Params &P, int rows, const int *slot_idx, int mode,
                        const Launch &ln) {
     const int pairs = rows * P.heads;
     if constexpr (D == 128) {
-        if (P.L <= 16)
-            wy_launch<V, D, T, 4, 2, 1>(P, pairs, slot_idx, mode, ln);
-        else if (P.L <= 32)
-            wy_launch<V, D, T, 4, 2, 2>(P, pairs, slot_idx, mode, ln);
-        else
+        if (P.L <= 16) {
+            if constexpr (V == GDN)
+                wy_launch<V, D, T, 4, 1, 1>(P, pairs, slot_idx, mode, ln);
+            else
+                wy_launch<V, D, T, 4, 2, 1>(P, pairs, slot_idx, mode, ln);
+        } else if (P.L <= 32) {
+            if constexpr (V == GDN)
+                wy_launch<V, D, T, 4, 1, 2>(P, pairs, slot_idx, mode, ln);
+            else
+                wy_launch<V, D, T, 4, 2, 2>(P, pairs, slot_idx, mode, ln);
+        } else {
             wy_launch<V, D, T, 4, 1, 4>(P, pairs, slot_idx, mode, ln);
+        }
     } else {
         wy_launch<V, D, T, 4, 1, 4>(P, pairs, slot_idx, mode, ln);
     }

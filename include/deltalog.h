@@ -361,6 +361,16 @@ int32_t dl_version(void);
  * for the descriptor with log_len = 1, or a NULL L_out. */
 dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_out);
 
+/* Whether the kernels of a state with this descriptor move its base with
+ * nontemporal (streaming) loads and stores: an eager state larger than the
+ * 256 MiB Infinity Cache, or a base and log together larger than 384 MiB
+ * (every log step reads both; streaming the base keeps the log entries
+ * cached).  A cache policy only: results are identical either way.  Host
+ * only, no GPU needed.  Writes 1 or 0 to *streams_out.  Errors:
+ * DL_ERR_INVALID / DL_ERR_UNSUPPORTED as dl_state_bytes would report for the
+ * descriptor, or a NULL streams_out. */
+dl_status dl_state_streams(const dl_desc *desc, int32_t *streams_out);
+
 /* Streaming-rate calibration, not part of the method: one launch that only
  * moves bytes, in the access pattern of the state kernels' largest stream
  * (16-byte nontemporal loads, 256 threads per workgroup), so that a kernel's

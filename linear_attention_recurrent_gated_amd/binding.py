@@ -74,6 +74,7 @@ _SIGS = {
     "dl_suggest_log_len": (_I, [ctypes.POINTER(DlDesc), ctypes.POINTER(ctypes.c_int32),
                                 ctypes.POINTER(ctypes.c_double)]),
     "dl_stream_probe": (_I, [_I, _P, _P, ctypes.c_size_t, _P, _P, _P]),
+    "dl_state_streams": (_I, [ctypes.POINTER(DlDesc), ctypes.POINTER(_I)]),
 }
 
 _lib = None
@@ -190,6 +191,13 @@ def dl_base_export(handle, rows, slot_idx, dst, stream) -> None:
 
 def dl_time_next_launch(handle, start_event, stop_event) -> None:
     _check(load().dl_time_next_launch(handle, start_event, stop_event))
+
+
+def dl_state_streams(desc: DlDesc) -> bool:
+    """Whether a state with this descriptor streams its base (cache policy)."""
+    out = _I(0)
+    _check(load().dl_state_streams(ctypes.byref(desc), ctypes.byref(out)))
+    return bool(out.value)
 
 
 def dl_stream_probe(mode, src, dst, nbytes, stream, start_event=None, stop_event=None) -> None:

@@ -126,6 +126,21 @@ Layout layout_of(const dl_desc &d) {
     return l;
 }
 
+// Stream the state (nontemporal loads and stores) when what the steps re-read
+// does not fit MI355X's 256 MiB Infinity Cache.  Eager: the state itself.
+// With a log, every step reads the whole base and the logged entries; once
+// base and log together are well past the cache (1.5x), streaming the base
+// keeps the log entries, read back by every step, resident instead of
+// letting both thrash.  The base is everything from the fp32 base (or the
+// INT8 codes, scales and kept channels) up to the log, the log everything
+// after it.
+bool streams(const dl_desc &d, const Layout &l) {
+    const size_t base_bytes = l.off_k - l.off_base;
+    const size_t log_bytes = l.total - l.off_k;
+    return d.log_len == 0 ? base_bytes > ((size_t)256 << 20)
+                          : base_bytes + log_bytes > ((size_t)384 << 20);
+}
+
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 dl_status check_rows(const dl_state *st, int32_t rows, const int32_t *slot_idx) {
@@ -253,16 +268,7 @@ dl_status dl_state_alloc(const dl_desc *desc, void *dev_mem, size_t bytes, void 
     p.rows = 0;
     p.row_order = nullptr;
     p.af = factors_form(*desc) ? 1 : 0;
-    // Stream the state (nontemporal loads and stores) when what the steps
-    // re-read does not fit MI355X's 256 MiB Infinity Cache.  Eager: the state
-    // itself.  With a log, every step reads the whole base and the logged
-    // entries; once base and log together are well past the cache (1.5x),
-    // streaming the base keeps the log entries, read back by every step,
-    // resident instead of letting both thrash.
-    const size_t base_bytes = (l.off_k - l.off_base) + (l.off_kidx - l.off_codes);
-    const size_t log_bytes = l.off_codes - l.off_k;
-    p.stream = desc->log_len == 0 ? base_bytes > ((size_t)256 << 20)
-                                  : base_bytes + log_bytes > ((size_t)384 << 20);
+    p.stream = streams(*desc, l);
     p.fill = reinterpret_cast<int *>(m + l.off_fill);
     p.q8 = desc->base_format == DL_BASE_I8 ? 1 : 0;
     p.M = p.q8 ? desc->kept_channels : 0;
@@ -527,6 +533,16 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
     *L_out = best;
     if (bytes_out)
         *bytes_out = best_bytes;
+    return ok();
+}
+
+dl_status dl_state_streams(const dl_desc *desc, int32_t *streams_out) {
+    if (!streams_out)
+        return fail(DL_ERR_INVALID, "streams_out must be non-NULL");
+    const dl_status cs = check_desc(desc);
+    if (cs != DL_OK)
+        return cs;
+    *streams_out = streams(*desc, layout_of(*desc)) ? 1 : 0;
     return ok();
 }
 

@@ -246,3 +246,26 @@ def test_stream_probe_rejects_bad_arguments():
     with pytest.raises(B.DlError) as e:
         B.dl_stream_probe(B.DL_PROBE_READ, buf, buf, 1024, None, start_event=buf)
     assert e.value.status == B.DL_ERR_INVALID
+
+
+def test_streaming_rule():
+    """The cache policy: an eager state streams above 256 MiB, a state with a
+    log once base and log together exceed 384 MiB (the log counts: a 256 MiB
+    base with a 160 MiB log streams)."""
+    def desc(variant, units, d, L, form=B.DL_LOG_FACTORS, base=B.DL_BASE_F32, M=0, fuse=1):
+        return B.DlDesc(variant, units, 32, d, d, L, B.DL_BF16, fuse if L else 0, form, base, M)
+    cases = [
+        (desc(B.DL_GDN, 64, 128, 16), False),               # 128 MiB base + 25 MiB log
+        (desc(B.DL_KDA, 128, 128, 0), False),               # eager, 256 MiB
+        (desc(B.DL_RWKV6, 1024, 64, 0), True),              # eager, 512 MiB (d = 64)
+        (desc(B.DL_KDA, 128, 128, 16), False),              # 256 + 80 MiB
+        (desc(B.DL_KDA, 128, 128, 32), True),               # 256 + 160 MiB
+        (desc(B.DL_KDA, 128, 128, 64), True),               # 256 + 320 MiB
+        (desc(B.DL_KDA, 128, 128, 32, form=B.DL_LOG_WY), True),   # 256 + 136 MiB
+        (desc(B.DL_GDN, 256, 128, 32), True),               # 512 MiB base
+        (desc(B.DL_KDA, 128, 128, 32, base=B.DL_BASE_I8, M=8), False),  # 82 + 160 MiB
+    ]
+    for d, want in cases:
+        assert B.dl_state_streams(d) == want, (d.variant, d.units, d.log_len, d.base_format)
+    with pytest.raises(B.DlError):
+        B.dl_state_streams(B.DlDesc(0, 1, 1, 96, 96, 0, B.DL_BF16))

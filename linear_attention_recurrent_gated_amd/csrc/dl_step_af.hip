@@ -156,6 +156,25 @@ __device__ __forceinline__ void af_merge_rows(const Params &P, size_t pair, int 
     }
 }
 
+// q8_kept_bits from the kept-channel indices the step has already loaded
+// (lane s: index s and s + 8) instead of a second read of the list, whose
+// wait would also wait for the base codes issued after it.
+template <int D>
+__device__ __forceinline__ uint32_t kept_bits_from_lanes(const int (&kc)[2], int M, int s, bool &ok) {
+    constexpr int QW = Q8Row<D>::QW;
+    uint32_t bits = 0u;
+    ok = true;
+    int prev = -1;
+    for (int m = 0; m < M; ++m) {
+        const int c = __builtin_amdgcn_readlane(m < 8 ? kc[0] : kc[1], m & 7);
+        ok = ok && c > prev && c < D;
+        prev = c;
+        if (c >= 0 && c < D && c / QW == s)
+            bits |= 1u << (c % QW);
+    }
+    return bits;
+}
+
 // This lane's codes of one INT8 base row (QW bytes), optionally nontemporal.
 template <int D, bool NT>
 __device__ __forceinline__ void load_codes(const int8_t *p, uint32_t *w) {
@@ -358,8 +377,12 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     if constexpr (Q8) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
+            // read unconditionally (index 0 past M; with M = 0 that is the
+            // first word after the indices, the log's, which an INT8 state
+            // always has), so that no wait for it lands before the codes
             const int m = s + 8 * i;
-            kc[i] = m < P.M ? P.kidx[h * P.M + m] : 0;
+            const int raw = P.kidx[h * P.M + (m < P.M ? m : 0)];
+            kc[i] = m < P.M ? raw : 0;
         }
 #pragma unroll
         for (int it = 0; it < SH::ITER; ++it) {
@@ -369,7 +392,9 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int m = s + 8 * i;
-                kv[it][i] = m < P.M ? P.kept[(pair * D + row) * P.M + m] : 0.f;
+                // unconditional, as the indices above (index 0 past M)
+                const float raw = P.kept[(pair * D + row) * P.M + (m < P.M ? m : 0)];
+                kv[it][i] = m < P.M ? raw : 0.f;
             }
         }
     } else {
@@ -395,7 +420,7 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     uint32_t kbits = 0u;
     if constexpr (Q8) {
         bool ok;
-        kbits = q8_kept_bits<D>(P, h, s, ok);
+        kbits = kept_bits_from_lanes<D>(kc, P.M, s, ok);
         if (!ok) {
             reject_row(P, orow, D, DL_FLAG_BAD_KEPT);
             return;
@@ -419,9 +444,10 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     const int ct = APPEND ? n + 1 : n;   // entries the readout sees
     const int npass = (ct + PASS - 1) / PASS;
     // logged entry j of pass p on this lane (clamped to the last logged one)
+    // (slot 0 of an empty log: a valid address whose data no lane uses)
     auto entry_of = [&](int p) {
         const int j = PASS * p + RP * wave + ro;
-        return e0 + (j < n ? j : n - 1);
+        return e0 + (j < n ? j : (n > 0 ? n - 1 : 0));
     };
     // Every pass gets its own registers (NP passes cover MV * 8 >= L
     // entries).  Before the barrier: two passes of keys (head-wise decay) or
@@ -429,11 +455,21 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     // right after it, all in flight together.
     constexpr int NP = (8 * MV + PASS - 1) / PASS;
     constexpr int EARLY = (V == GDN && NP > 1) ? 2 : 1;
-    KeyRaw pre[NP];
+    // Over an INT8 base every pass is loaded whatever the fill (passes past
+    // the log read its last entry again, a cache hit, and are never used): a
+    // load under a condition leaves its result to be merged with the other
+    // branch's value, and the compiler waits for every load in flight (the
+    // base codes included) before that copy, which holds back the factor
+    // staging (C4 INT8 step 106 -> 93 us with the kept-channel reads below).
+    // With an fp32 base the same change measured no faster and slower for
+    // per-key decays at 64 entries, so there the passes stay conditional.
+    KeyRaw pre[NP] = {};
+    if constexpr (Q8) {
 #pragma unroll
-    for (int p = 0; p < NP; ++p)
-        pre[p] = KeyRaw{};
-    if (n > 0) {
+        for (int p = 0; p < EARLY; ++p)
+            load_key_raw<V, D, T>(P, entry_of(p), ch0, pre[p]);
+        af_stage_factors(P, pair, n, D, smem, ap, lane, wave);
+    } else if (n > 0) {
 #pragma unroll
         for (int p = 0; p < EARLY; ++p)
             if (p < npass)
@@ -535,7 +571,11 @@ af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__
     float ekv[8];                        // gated: this lane's channels of e * k
     if constexpr (APPEND && V == GDN2)
         load8<float>(reinterpret_cast<const float *>(smem + ap.off_ek) + chl, ekv);
-    if (n > 0) {
+    if constexpr (Q8) {
+#pragma unroll
+        for (int p = EARLY; p < NP; ++p)
+            load_key_raw<V, D, T>(P, entry_of(p), chl, pre[p]);
+    } else if (n > 0) {
 #pragma unroll
         for (int p = EARLY; p < NP; ++p)
             if (p < npass)

@@ -256,7 +256,7 @@ def parse_args(argv=None):
     ap.add_argument("--config", type=int, default=4, choices=sorted(W.WORKLOADS))
     ap.add_argument("--L", type=int, default=None, help="log slots (default: the workload's)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--reps", type=int, default=3,
+    ap.add_argument("--reps", type=int, default=5,
                     help="timed repetitions of the K steps (each from the same state); "
                          "value is the median")
     ap.add_argument("--paths", default="eager,log,log-fused,af,af-fused,af-fused-i8",

@@ -520,8 +520,10 @@ dl_status dl_suggest_log_len(const dl_desc *desc, int32_t *L_out, double *bytes_
         // merging in place writes the base once per L steps and saves that
         // step's append; a separate merge reads and writes the base and reads the log
         bytes += fuse ? (St - E) / L : (2.0 * St + L * E + 8.0) / L;
-        const int lds = af ? dl::af_plan(d.d_k, L, fuse).bytes
-                           : dl::step_plan(d.variant, d.d_k, (int)es, L, fuse).bytes;
+        const bool chunked = !af && d.variant == DL_KDA && d.d_k == 128 && L > 32 && !fuse;
+        const int lds = af        ? dl::af_plan(d.d_k, L, fuse).bytes
+                        : chunked ? dl::chunk_plan(d.d_k, (int)es, L).bytes
+                                  : dl::step_plan(d.variant, d.d_k, (int)es, L, fuse).bytes;
         const int wgs = std::min(4, (160 * 1024) / std::max(lds, 1));
         const double cost = bytes * 4.0 / std::max(wgs, 1);
         if (L == 1 || cost < best_cost) {

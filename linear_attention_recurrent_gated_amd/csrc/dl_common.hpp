@@ -279,6 +279,45 @@ __host__ __device__ inline StepPlan step_plan(int variant, int D, int esize, int
     return p;
 }
 
+// LDS carve-up of the chunked compact-WY step (per-key decays at d = 128,
+// logs of 33 to 64 entries, no merge in the step): keys and decays of 32
+// entries at a time, the values later in their place, the appended entry on
+// its own, R whole.
+struct ChunkPlan {
+    int off_kc;    // keys of one chunk: 32 rows of D elements (input dtype)
+    int off_lc;    // cumulative log-decays of that chunk: 32 rows of D floats
+    int off_v;     // after q0: the logged values, rows of D elements (over kc, lc)
+    int off_kn, off_ln, off_vn;       // the appended entry's key, decays, value
+    int off_t;     // packed columns of R
+    int off_r, off_u, off_f;          // per-entry scalars, 64 floats each
+    int off_bn;    // beta of the appended entry
+    int off_c;     // per-wave coefficients, 4 x 64 floats
+    int off_qin, off_q;               // q as floats and q0, D floats each
+    int bytes;
+};
+
+__host__ __device__ inline ChunkPlan chunk_plan(int D, int esize, int L) {
+    ChunkPlan p;
+    p.off_kc = 0;
+    p.off_lc = round_up(32 * D * esize, 256);
+    p.off_v = 0;
+    const int chunk_end = p.off_lc + round_up(32 * D * 4, 256);
+    const int values_end = round_up(L * D * esize, 256);
+    p.off_kn = chunk_end > values_end ? chunk_end : values_end;
+    p.off_ln = p.off_kn + round_up(D * esize, 16);
+    p.off_vn = p.off_ln + D * 4;
+    p.off_t = round_up(p.off_vn + D * esize, 256);
+    p.off_r = p.off_t + round_up(packed_t_len(DL_KDA, L) * 4, 256);
+    p.off_u = p.off_r + 256;
+    p.off_f = p.off_u + 256;
+    p.off_bn = p.off_f + 256;
+    p.off_c = p.off_bn + 16;
+    p.off_qin = p.off_c + 4 * 256;
+    p.off_q = p.off_qin + D * 4;
+    p.bytes = p.off_q + D * 4;
+    return p;
+}
+
 // e^x through the hardware base-2 exponential: about 1 ulp plus the rounding
 // of x log2(e) (relative error near |x| 2^-24); results below the normal
 // range flush to zero.

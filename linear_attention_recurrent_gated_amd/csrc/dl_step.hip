@@ -801,6 +801,365 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Chunked compact-WY step for per-key decays at d = 128 with logs of 33 to 64
+// entries (no merge in the step).  The same arithmetic as log_step_kernel,
+// but its 64 staged keys, values and decay rows (72 KiB of LDS, two
+// workgroups per CU) become 32 keys and decay rows at a time, the values
+// staged in their place once q0 is formed and the appended entry kept apart:
+// 36 KiB, four workgroups per CU.  The dot products run over the first 32
+// entries, then the rest once they are staged; q0 over the entries still
+// staged, then over the first 32 staged again; the readout after the values.
+// ---------------------------------------------------------------------------
+
+// Direct-to-LDS staging of rows [j0, j0 + cnt) of a log array of `row`
+// 16-byte chunks per entry into `dst` (this wave's batches of 64 lanes).
+__device__ __forceinline__ void stage_rows(const void *base, size_t e0, int j0, int cnt, int row,
+                                           unsigned char *dst, int lane, int wave) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(base) + (e0 + j0) * row;
+    const int nchunk = cnt * row;
+    for (int b = 64 * wave; b < nchunk; b += 256) {
+        const int idx = b + lane;
+        if (idx < nchunk)
+            load_to_lds<16>(src + idx, dst + 16 * b);
+    }
+}
+
+template <int D, typename T, bool APPEND, bool NT>
+__global__ void __launch_bounds__(256, 4)
+log_step_chunked_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
+                        const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
+                        const float *__restrict__ beta, float *__restrict__ o) {
+    using SH = Shape<D>;
+    using KL = KeyLayout<D>;
+    constexpr int G = KL::G, RP = KL::RP, PASS = 4 * RP;   // entries per pass of the four waves
+    constexpr int CH = 32;                                // entries per staged chunk
+    constexpr int MV = 8;                                 // value entries per lane per row
+    constexpr int KROW = D * (int)sizeof(T) / 16;         // 16-byte chunks per key / value row
+    constexpr int LROW = D / 4;                           // 16-byte chunks per decay row
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int H = P.heads, L = P.L;
+    int h;
+    const int r = step_row(P, h);
+    if (r < 0) {
+        reject_row(P, nullptr, D, DL_FLAG_BAD_SLOT);
+        return;
+    }
+    const int pr = r * H + h;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float *orow = o + (size_t)pr * D;
+    const int unit = slot_idx ? slot_idx[r] : r;
+    if (unit < 0 || unit >= P.units) {
+        reject_row(P, orow, D, DL_FLAG_BAD_SLOT);
+        return;
+    }
+    const size_t pair = (size_t)unit * H + h;
+    const size_t io = (size_t)pr * D;
+    const size_t e0 = pair * L;
+    const ChunkPlan cp = chunk_plan(D, (int)sizeof(T), L);
+    float *sT = reinterpret_cast<float *>(smem + cp.off_t);
+    float *sr = reinterpret_cast<float *>(smem + cp.off_r);
+    float *su = reinterpret_cast<float *>(smem + cp.off_u);
+    float *sf = reinterpret_cast<float *>(smem + cp.off_f);
+    float *sb_new = reinterpret_cast<float *>(smem + cp.off_bn);
+    float *sc = reinterpret_cast<float *>(smem + cp.off_c) + 64 * wave;
+    float *sq = reinterpret_cast<float *>(smem + cp.off_q);
+    float *sqin = reinterpret_cast<float *>(smem + cp.off_qin);
+    float *sln = reinterpret_cast<float *>(smem + cp.off_ln);   // Lam_c (the appended entry's, or the newest's)
+
+    // ---- loads that need nothing: fill, this wave's rows of S0, the inputs
+    const int n = P.fill[pair];
+    const int grp = lane >> 3, s = lane & 7;
+    const float *Sp = P.base + pair * D * D;
+    float4 st[SH::ITER][SH::NCH];
+#pragma unroll
+    for (int it = 0; it < SH::ITER; ++it) {
+        const int row = wave * SH::RPW + it * 8 + grp;
+#pragma unroll
+        for (int m = 0; m < SH::NCH; ++m)
+            st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
+    }
+    const int cg = lane % G, ro = lane / G, ch0 = 8 * cg;
+    float qv[8], kn[8];
+    load8<T>(q + io + ch0, qv);
+    if constexpr (APPEND)
+        load8<T>(k + io + ch0, kn);
+    __builtin_amdgcn_sched_barrier(0);
+    if (APPEND ? (n >= L || n < 0) : (n > L || n < 0)) {
+        reject_row(P, orow, D, DL_FLAG_LOG_FULL);
+        return;
+    }
+    const int ct = APPEND ? n + 1 : n;       // entries the readout sees
+    const int na = n < CH ? n : CH;          // logged entries in the first chunk
+
+    // ---- loads that need n: this lane's rows of the new value, the first
+    //      chunk and R, and (wave 0) the per-entry scalars and the append
+    float vc[SH::ITER];
+#pragma unroll
+    for (int it = 0; it < SH::ITER; ++it)
+        vc[it] = APPEND ? Elem<T>::load1(v + io + wave * SH::RPW + it * 8 + grp) : 0.f;
+    stage_rows(P.log_k, e0, 0, na, KROW, smem + cp.off_kc, lane, wave);
+    stage_rows(P.log_g, e0, 0, na, LROW, smem + cp.off_lc, lane, wave);
+    {
+        const int nt = n * (n - 1) / 2;
+        const float *ts = P.log_t + pair * packed_t_len(DL_KDA, L);
+        for (int b = 64 * wave; b < nt; b += 256)
+            if (b + lane < nt)
+                load_to_lds<4>(ts + b + lane, smem + cp.off_t + 4 * b);
+    }
+    if (wave == 0) {
+        const int jl = lane < n ? lane : (n > 0 ? n - 1 : 0);
+        float b_j = 1.f, lc[8], b_in = 1.f, gn[8], vv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            lc[i] = 0.f;
+        if (n > 0) {
+            b_j = P.log_beta[e0 + jl];
+            load8<float>(P.log_g + (e0 + n - 1) * D + ch0, lc);
+        }
+        if constexpr (APPEND) {
+            load8<T>(v + io + ch0, vv);
+            load8<float>(g + io + ch0, gn);
+            b_in = beta[pr];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                lc[i] += gn[i];
+        }
+        if (ro == 0) {
+            store8<float>(sln + ch0, lc);      // Lam_c
+            if constexpr (APPEND) {
+                store8<T>(reinterpret_cast<T *>(smem + cp.off_kn) + ch0, kn);
+                store8<T>(reinterpret_cast<T *>(smem + cp.off_vn) + ch0, vv);
+            }
+            store8<float>(sqin + ch0, qv);
+        }
+        if constexpr (APPEND) {
+            if (lane == 0)
+                sb_new[0] = b_in;
+            if (lane == n)
+                b_j = b_in;
+        }
+        if (lane < ct)
+            sf[lane] = b_j;
+    }
+    wait_vm_all();
+    __syncthreads();    // 1: the first chunk, R, the new entry, per-entry factors
+
+    // key and decay rows of entry j: the appended entry's own copies, or
+    // row j - c0 of the staged chunk
+    auto krow = [&](int j, int c0) {
+        return (APPEND && j == n) ? reinterpret_cast<const T *>(smem + cp.off_kn)
+                                  : reinterpret_cast<const T *>(smem + cp.off_kc) + (j - c0) * D;
+    };
+    auto lrow = [&](int j, int c0) {
+        return (APPEND && j == n) ? static_cast<const float *>(sln)
+                                  : reinterpret_cast<const float *>(smem + cp.off_lc) + (j - c0) * D;
+    };
+    float lc[8];
+    load8<float>(sln + ch0, lc);
+
+    // ---- r_j = f_j k_j.(D q) and u_j = f_j k_j.(D k_n): passes 0, 1 over the
+    //      first chunk, passes 2, 3 over the second once it is staged
+    auto dots = [&](int p, int c0) {
+        const int j = PASS * p + RP * wave + ro;
+        const int jc = j < ct ? j : ct - 1;
+        float kr[8], lr[8];
+        load8<T>(krow(jc, c0) + ch0, kr);
+        load8<float>(lrow(jc, c0) + ch0, lr);
+        const float fr = sf[jc];
+        float ar = 0.f, au = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float kd = kr[i] * fast_exp(lc[i] - lr[i]);
+            ar += kd * qv[i];
+            if constexpr (APPEND)
+                au += kd * kn[i];
+        }
+        ar = group_sum<G>(ar);
+        if constexpr (APPEND)
+            au = group_sum<G>(au);
+        if (cg == 0 && j < ct) {
+            sr[j] = fr * ar;
+            if constexpr (APPEND)
+                su[j] = fr * au;
+        }
+    };
+    const int npass = (ct + PASS - 1) / PASS;
+    for (int p = 0; p < 2 && p < npass; ++p)
+        dots(p, 0);
+    if (ct > CH) {
+        __syncthreads();    // every wave is done with the first chunk
+        stage_rows(P.log_k, e0, CH, n - CH, KROW, smem + cp.off_kc, lane, wave);
+        stage_rows(P.log_g, e0, CH, n - CH, LROW, smem + cp.off_lc, lane, wave);
+        wait_vm_all();
+        __syncthreads();    // the second chunk
+        for (int p = 2; p < npass; ++p)
+            dots(p, CH);
+    }
+    __syncthreads();    // 2: r and u of every entry
+
+    // ---- lane i: the new column R[i, n] and coef_i = (R r)_i (every wave
+    //      for itself; wave 0 stores the new column)
+    float coef = 0.f;
+    if (lane < ct) {
+        const int i = lane;
+        coef = sr[i];
+        float acc_u = APPEND ? su[i] : 0.f;
+        const int mend = APPEND ? n : ct;     // stored columns m < mend
+        for (int m0 = 0; m0 < mend; m0 += 8) {
+            float rv[8], uv[8], Rv[8];
+#pragma unroll
+            for (int t = 0; t < 8; t += 4) {
+                const float4 a = *reinterpret_cast<const float4 *>(sr + m0 + t);
+                const float ra[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    rv[t + e] = (m0 + t + e < mend) ? ra[e] : 0.f;
+                if constexpr (APPEND) {
+                    const float4 b = *reinterpret_cast<const float4 *>(su + m0 + t);
+                    const float ub[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        uv[t + e] = (m0 + t + e < mend) ? ub[e] : 0.f;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int m = m0 + t;
+                const int lim = m < mend ? m : 0;
+                const int col = m < mend ? m * (m - 1) / 2 : 0;
+                Rv[t] = sT[col + (i < lim ? i : 0)];
+                Rv[t] = i < lim ? Rv[t] : 0.f;
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                coef += Rv[t] * rv[t];
+                if constexpr (APPEND)
+                    acc_u += Rv[t] * uv[t];
+            }
+        }
+        if constexpr (APPEND) {
+            if (i < n) {
+                const float w = -acc_u;
+                if (wave == 0)
+                    sT[n * (n - 1) / 2 + i] = w;
+                coef += w * sr[n];
+            }
+        }
+    }
+    if (lane < PASS * npass)
+        sc[lane] = coef;
+    wave_lds_sync();
+
+    // ---- q0 = E_c q - sum_j coef_j E_j k_j on this wave's quarter of the
+    //      channels: over the entries of the staged chunk, then (longer logs)
+    //      over the first chunk staged again
+    constexpr int LQ = D / 32, RQ = 64 / LQ;
+    const int c4 = lane % LQ, jr = lane / LQ;
+    const int chq = (D / 4) * wave + 8 * c4;
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] = 0.f;
+    auto q0_part = [&](int jbeg, int jend, int c0) {
+        for (int p = jbeg; p < jend; p += RQ) {
+            const int j = p + jr;
+            const int jc = j < ct ? j : ct - 1;
+            float kr[8], lr[8];
+            load8<T>(krow(jc, c0) + chq, kr);
+            load8<float>(lrow(jc, c0) + chq, lr);
+            const float cr = j < jend ? sc[jc] : 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                acc[i] += cr * kr[i] * fast_exp(lr[i]);
+        }
+    };
+    if (ct > CH) {
+        q0_part(CH, ct, CH);
+        __syncthreads();    // every wave is done with the second chunk
+        stage_rows(P.log_k, e0, 0, CH, KROW, smem + cp.off_kc, lane, wave);
+        stage_rows(P.log_g, e0, 0, CH, LROW, smem + cp.off_lc, lane, wave);
+        wait_vm_all();
+        __syncthreads();    // the first chunk again
+        q0_part(0, CH, 0);
+    } else {
+        q0_part(0, ct, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] = sum_mod<LQ>(acc[i]);
+    if (jr == 0) {
+        float qq[8], lq[8], out[8];
+        load8<float>(sqin + chq, qq);
+        load8<float>(sln + chq, lq);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            out[i] = fast_exp(lq[i]) * qq[i] - acc[i];
+        store8<float>(sq + chq, out);
+    }
+    __syncthreads();    // 3: q0; the chunks are free
+
+    // ---- the logged values, in the chunks' place
+    stage_rows(P.log_v, e0, 0, n, KROW, smem + cp.off_v, lane, wave);
+    wait_vm_all();
+    __syncthreads();    // 4: values
+
+    // ---- o = S0 q0 + sum_j coef_j v_j for this wave's rows
+    const T *vrows = reinterpret_cast<const T *>(smem + cp.off_v);
+    float qt[SH::FPL];
+#pragma unroll
+    for (int m = 0; m < SH::NCH; ++m)
+        f4_to(qt + 4 * m, *reinterpret_cast<const float4 *>(sq + col_of(s, m, 0)));
+    float cf[MV];
+#pragma unroll
+    for (int mm = 0; mm < MV; ++mm) {
+        const int j = s + 8 * mm;
+        cf[mm] = (j < n) ? sc[j < n ? j : 0] : 0.f;
+    }
+    const float ccur = (APPEND && s == 0) ? sc[n] : 0.f;
+#pragma unroll
+    for (int it = 0; it < SH::ITER; ++it) {
+        const int row = wave * SH::RPW + it * 8 + grp;
+        float acc_o = 0.f;
+#pragma unroll
+        for (int m = 0; m < SH::NCH; ++m)
+            acc_o += st[it][m].x * qt[4 * m] + st[it][m].y * qt[4 * m + 1] +
+                     st[it][m].z * qt[4 * m + 2] + st[it][m].w * qt[4 * m + 3];
+#pragma unroll
+        for (int mm = 0; mm < MV; ++mm) {
+            const int j = s + 8 * mm;
+            const float x = Elem<T>::load1(vrows + (j < n ? j : 0) * D + row);
+            acc_o += cf[mm] * (j < n ? x : 0.f);
+        }
+        if (APPEND)
+            acc_o += ccur * vc[it];
+        acc_o = sum8(acc_o);
+        if (s == 0)
+            orow[row] = acc_o;
+    }
+
+    // ---- append entry n: k and v (bit copies), Lam_n, beta, column n of R
+    if constexpr (APPEND) {
+        if (wave == 0) {
+            const size_t e = e0 + n;
+            if (lane < KROW) {
+                reinterpret_cast<uint4 *>(static_cast<T *>(P.log_k) + e * D)[lane] =
+                    reinterpret_cast<const uint4 *>(smem + cp.off_kn)[lane];
+                reinterpret_cast<uint4 *>(static_cast<T *>(P.log_v) + e * D)[lane] =
+                    reinterpret_cast<const uint4 *>(smem + cp.off_vn)[lane];
+            }
+            if (lane < LROW)
+                reinterpret_cast<float4 *>(P.log_g + e * D)[lane] = reinterpret_cast<const float4 *>(sln)[lane];
+            if (lane == 0)
+                P.log_beta[e] = sb_new[0];
+            if (lane < n)
+                P.log_t[pair * packed_t_len(DL_KDA, L) + n * (n - 1) / 2 + lane] = sT[n * (n - 1) / 2 + lane];
+        }
+        if (tid == 0)
+            P.fill[pair] = n + 1;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 #define DL_DISPATCH(P, FN, ...)                                                          \
@@ -883,6 +1242,21 @@ template <int V, int D, typename T, bool APPEND>
 static hipError_t log_t(const Params &P, int rows, const int *slot_idx, const void *q,
                         const void *k, const void *v, const float *g, const float *beta,
                         float *o, const Launch &ln) {
+    // per-key decays at d = 128 with more than 32 entries and no merge in the
+    // step: the chunked kernel (four workgroups per CU instead of two)
+    if constexpr (V == KDA && D == 128) {
+        if (P.L > 32 && !(APPEND && P.fuse)) {
+            const ChunkPlan cp = chunk_plan(D, (int)sizeof(T), P.L);
+            const dim3 grid(rows * P.heads), block(256);
+#define DL_CHUNK_LAUNCH(NTV)                                                                          \
+    hipExtLaunchKernelGGL((log_step_chunked_kernel<D, T, APPEND, NTV>), grid, block, cp.bytes, ln.stream, \
+                          ln.start, ln.stop, 0, P, slot_idx, static_cast<const T *>(q),               \
+                          static_cast<const T *>(k), static_cast<const T *>(v), g, beta, o)
+            if (P.stream) DL_CHUNK_LAUNCH(true); else DL_CHUNK_LAUNCH(false);
+#undef DL_CHUNK_LAUNCH
+            return hipGetLastError();
+        }
+    }
     // MV = value-log entries per lane per row = ceil(L / 8), rounded up to 2, 4 or 8
     if (P.L <= 16)
         log_launch<V, D, T, APPEND, 2>(P, rows, slot_idx, q, k, v, g, beta, o, ln);

@@ -128,20 +128,24 @@ def test_factor_log_payload(wl, L, path):
     run_case(wl, L, (path,), merge_every_step=True, run_oracle=False, on_step=on_step)
 
 
-_READOUT_CASES = [(w, f) for w in (W.GDN_HYBRID.scaled(batch=2, heads=3, steps=20),
-                                    W.KDA_SWEEP.scaled(batch=2, heads=3, steps=20),
-                                    W.RWKV6_ADD.scaled(batch=2, heads=3, steps=20),
-                                    W.GATED.scaled(batch=2, heads=3, steps=20))
+_READOUT_CASES = [(w, f, 6, (0, 3, 5, 8, 13, 19))
+                  for w in (W.GDN_HYBRID.scaled(batch=2, heads=3, steps=20),
+                            W.KDA_SWEEP.scaled(batch=2, heads=3, steps=20),
+                            W.RWKV6_ADD.scaled(batch=2, heads=3, steps=20),
+                            W.GATED.scaled(batch=2, heads=3, steps=20))
                   for f in (B.DL_LOG_WY, B.DL_LOG_FACTORS)
                   if not (w.variant == W.GDN2 and f == B.DL_LOG_WY)]   # gated: factor log only
+# per-key decays with a log longer than 32 entries (the WY readout stages its
+# entries 32 at a time): readouts with 21, 35 and 39 entries, and after a merge
+_READOUT_CASES += [(W.KDA_SWEEP.scaled(batch=2, heads=3, steps=46), f, 40, (20, 34, 38, 45))
+                   for f in (B.DL_LOG_WY, B.DL_LOG_FACTORS)]
 
 
-@pytest.mark.parametrize("wl,form", _READOUT_CASES,
-                         ids=[f"{('gdn', 'kda', 'rwkv6', 'gated')[w.variant]}-{'factors' if f else 'wy'}"
-                              for w, f in _READOUT_CASES])
-def test_readout_matches_oracle(wl, form):
+@pytest.mark.parametrize("wl,form,L,taus", _READOUT_CASES,
+                         ids=[f"{('gdn', 'kda', 'rwkv6', 'gated')[w.variant]}-{'factors' if f else 'wy'}-L{L}"
+                              for w, f, L, _ in _READOUT_CASES])
+def test_readout_matches_oracle(wl, form, L, taus):
     """dl_readout returns S_t q for a fresh q, mid-log and after merges, and changes nothing."""
-    L = 6
     H, d = wl.heads, wl.d_k
     P = wl.batch * H
     log(f"case readout {wl.name} form={form}")
@@ -159,7 +163,7 @@ def test_readout_matches_oracle(wl, form):
         eg.step_eager(*args)
         if (tau + 1) % L == 0:
             st.merge(B.DL_MERGE_FULL)
-        if tau in (0, 3, L - 1, L + 2, 2 * L + 1, wl.steps - 1):
+        if tau in taus:
             qn = rng.standard_normal((wl.batch, H, d))
             qs, qf = W.store(qn, wl.dtype)
             qt = to_torch(qs, wl.dtype)

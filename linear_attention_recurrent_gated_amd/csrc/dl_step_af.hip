@@ -305,10 +305,14 @@ __device__ __forceinline__ void af_merge_rows_q8(const Params &P, size_t pair, i
 // entries the kernel is held to the registers of four waves per SIMD (four
 // workgroups per CU), except where that spills on the hot path (32 entries
 // with per-key decays and the merge in the step, or with gates), which runs
-// three.
+// three.  Over an INT8 base, whose codes take a quarter of the registers,
+// logs of up to 16 entries run five (the build that merges in place keeps
+// one value per lane in scratch across the barriers, and still gains 2-3%;
+// the gated form measured slower at five).
 template <int V, int D, typename T, bool APPEND, int MV, bool NT, bool FUSE, bool Q8>
 __global__ void __launch_bounds__(256, (MV <= 4 && sizeof(T) == 2)
-                                          ? (Q8 ? 4 : ((MV == 4 && (V == GDN2 || (V == KDA && FUSE))) ? 3 : 4))
+                                          ? (Q8 ? ((MV == 2 && V != GDN2) ? 5 : 4)
+                                                : ((MV == 4 && (V == GDN2 || (V == KDA && FUSE))) ? 3 : 4))
                                           : 1)
 af_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict__ q,
                const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,

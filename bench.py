@@ -157,11 +157,39 @@ def merge_flops(wl, n, factors=False):
 
 
 # ---------------------------------------------------------------------------
-def source_hash() -> str:
+# The sources a kernel's counters depend on: the file that holds the kernel
+# and its launch, plus what every kernel shares (the common device code, the
+# C ABI with the state layout, the public header).  A summary stays valid
+# while these files are unchanged, so a change to one kernel's file leaves the
+# other kernels' counters standing.
+KERNEL_SOURCES = {
+    "eager_step_kernel": ("dl_step.hip",),
+    "log_step_kernel": ("dl_step.hip",),
+    "af_step_kernel": ("dl_step_af.hip",),
+    "af_merge_kernel": ("dl_step_af.hip",),
+    "merge_wy_kernel": ("dl_merge.hip",),
+    "stream_probe": ("dl_probe.hip",),
+}
+SHARED_SOURCES = ("dl_common.hpp", "dl_abi.hip")
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """sha256 (first 16 hex digits) of the sources behind ``kernel`` (its base
+    name, before any '.'), or of every source file when it is None or not a
+    kernel listed above."""
+    csrc = os.path.join(ROOT, "linear_attention_recurrent_gated_amd", "csrc")
+    base = kernel.split(".")[0] if kernel else None
+    if base in KERNEL_SOURCES:
+        files = [os.path.join(csrc, f) for f in sorted(SHARED_SOURCES + KERNEL_SOURCES[base])]
+        files.append(os.path.join(ROOT, "include", "deltalog.h"))
+    else:
+        files = sorted(glob.glob(os.path.join(csrc, "*")))
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "linear_attention_recurrent_gated_amd", "csrc", "*"))):
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for p in files:
+        h.update(os.path.basename(p).encode() + b"\0")
+        if os.path.exists(p):
+            with open(p, "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -177,7 +205,7 @@ def counter_field(kernel: str, workload: str, field: str, log_len: int | None = 
             if ":" in line and line.startswith("- "):
                 k, v = line[2:].split(":", 1)
                 vals[k.strip()] = v.strip().strip("`")
-    if vals.get("source_sha256_16") != source_hash():
+    if vals.get("source_sha256_16") != source_hash(kernel):
         return None
     if log_len is not None and vals.get("log_len") not in (None, str(log_len)):
         return None

@@ -54,17 +54,40 @@ def _write_summary(root, kernel, workload, src, traffic, log_len=None):
 def test_counter_traffic_matches_sources_and_log_len(tmp_path, monkeypatch):
     csrc = tmp_path / "linear_attention_recurrent_gated_amd" / "csrc"
     csrc.mkdir(parents=True)
-    (csrc / "k.hip").write_text("kernel v1\n")
+    for name in ("dl_step_af.hip", "dl_step.hip", "dl_merge.hip", "dl_common.hpp", "dl_abi.hip"):
+        (csrc / name).write_text(f"{name} v1\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    src = bench.source_hash()
-    _write_summary(str(tmp_path), "af_step_kernel", "wl", src, 1234, log_len=16)
-    _write_summary(str(tmp_path), "eager_step_kernel", "wl", src, 99)
+    _write_summary(str(tmp_path), "af_step_kernel", "wl", bench.source_hash("af_step_kernel"), 1234, log_len=16)
+    _write_summary(str(tmp_path), "eager_step_kernel", "wl", bench.source_hash("eager_step_kernel"), 99)
+    _write_summary(str(tmp_path), "merge_wy_kernel", "wl", bench.source_hash("merge_wy_kernel"), 7)
     assert bench.counter_traffic("af_step_kernel", "wl", 16) == 1234.0
     assert bench.counter_traffic("af_step_kernel", "wl", 8) is None      # taken at another L
     assert bench.counter_traffic("eager_step_kernel", "wl", 8) == 99.0   # no log, any L
     assert bench.counter_traffic("missing_kernel", "wl", 16) is None
-    (csrc / "k.hip").write_text("kernel v2\n")                            # sources changed
+    # a change to one kernel's file voids that kernel's counters only
+    (csrc / "dl_merge.hip").write_text("dl_merge.hip v2\n")
+    assert bench.counter_traffic("merge_wy_kernel", "wl") is None
+    assert bench.counter_traffic("af_step_kernel", "wl", 16) == 1234.0
+    assert bench.counter_traffic("eager_step_kernel", "wl") == 99.0
+    # the step kernels' own file
+    (csrc / "dl_step_af.hip").write_text("dl_step_af.hip v2\n")
     assert bench.counter_traffic("af_step_kernel", "wl", 16) is None
+    assert bench.counter_traffic("eager_step_kernel", "wl") == 99.0
+    # shared sources void every summary
+    (csrc / "dl_common.hpp").write_text("dl_common.hpp v2\n")
+    assert bench.counter_traffic("eager_step_kernel", "wl") is None
+
+
+def test_committed_summaries_name_their_kernels_sources():
+    """Every committed summary carries the hash of the sources behind its
+    kernel (so bench.py reports its traffic), as long as those are unchanged."""
+    import glob
+    for f in sorted(glob.glob(os.path.join(os.path.dirname(bench.__file__), "profiles", "*.md"))):
+        kernel = os.path.basename(f).split(".")[0]
+        assert kernel in bench.KERNEL_SOURCES, f
+        with open(f) as fh:
+            hashes = {ln.split("`")[1] for ln in fh if ln.startswith("- source_sha256_16:")}
+        assert len(hashes) == 1, f
 
 
 @pytest.mark.parametrize("cfg", sorted(W.WORKLOADS))

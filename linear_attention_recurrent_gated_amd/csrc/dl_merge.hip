@@ -445,6 +445,354 @@ merge_wy_kernel(Params P, const int *__restrict__ slot_idx, int mode, int npairs
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// WY merge for long logs at d = 128 (more than 32 entries): the same
+// products as merge_wy_kernel, with the key side staged 16 entries at a time
+// instead of whole.  A log of 64 entries with per-key decays has 48 KiB of
+// keys and decays; staged whole beside R they leave room for two workgroups
+// per CU, staged a chunk at a time (double-buffered: the next chunk loads
+// while this one is used) for four.  Everything that needs the key side is
+// done while its chunk is in LDS:
+//   phase A  z_c = V_c^T - S0 Kt_c^T            (chunk c's keys),
+//   Y        Y_t += R[t, c] Q_c for every t <= c (R is upper triangular, so
+//            chunk c's entries reach the rows of Y up to chunk c),
+// with the Y_t of every chunk accumulating in registers (each wave its share
+// of the column blocks); then S0 diag(E_c) + sum_t z_t Y_t as before, each
+// Y_t passing through LDS.  R stays whole in LDS (8 KiB at 64 entries), and
+// the Lam row of the last entry, which every D(i, c) needs, is staged apart.
+// A pair's rows split over two workgroups (64 rows each).
+// ---------------------------------------------------------------------------
+struct WyChunkPlan {
+    int off_t;     // packed columns of R, whole log
+    int off_buf;   // two staging buffers of one 16-entry chunk: keys, then Lam
+    int buf;       // bytes per buffer
+    int lam;       // offset of Lam inside a buffer
+    int off_y;     // one chunk of Y, 16 rows of D + 4 floats (over the buffers)
+    int off_ll;    // per-key decays: Lam of the last entry, D floats
+    int off_f;     // per entry: beta_j (head-wise decay: times D(j, c)), 64 floats
+    int off_e;     // per entry (head-wise decay): E_j, 64 floats
+    int off_ec;    // E_c per key channel, D floats
+    int off_n;     // the fill count read by the workgroup
+    int bytes;
+};
+
+__host__ __device__ inline WyChunkPlan wy_chunk_plan(int variant, int D, int esize, int L) {
+    WyChunkPlan p;
+    p.off_t = 0;
+    p.off_buf = round_up(packed_t_len(variant, L) * 4, 256);
+    p.lam = round_up(16 * D * esize, 256);
+    const int stage = p.lam + (variant == DL_GDN ? 0 : round_up(16 * D * 4, 256));
+    const int ybytes = round_up(16 * (D + 4) * 4, 256);
+    p.buf = stage;
+    p.off_y = p.off_buf;
+    const int end = p.off_buf + (2 * stage > ybytes ? 2 * stage : ybytes);
+    p.off_ll = end;
+    p.off_f = p.off_ll + (variant == DL_GDN ? 0 : D * 4);
+    p.off_e = p.off_f + 256;
+    p.off_ec = p.off_e + 256;
+    p.off_n = p.off_ec + D * 4;
+    p.bytes = p.off_n + 16;
+    return p;
+}
+
+template <int V, int D, typename T, bool NTS>
+__global__ void __launch_bounds__(256, 4)
+merge_wy_chunked_kernel(Params P, const int *__restrict__ slot_idx, int mode, int npairs) {
+    static_assert(D == 128, "long-log WY merge at d = 128");
+    constexpr int NW = 4, ROWS = 16 * NW, NS = D / ROWS, NM = D / 16, KS = D + 4, MAXC = 4;
+    constexpr bool PK = V != GDN, DELTA = V != RWKV6;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int L = P.L;
+    const WyChunkPlan wp = wy_chunk_plan(V, D, (int)sizeof(T), L);
+    const float *sT = reinterpret_cast<const float *>(smem + wp.off_t);
+    const float *sll = reinterpret_cast<const float *>(smem + wp.off_ll);
+    float *sf = reinterpret_cast<float *>(smem + wp.off_f);
+    float *se = reinterpret_cast<float *>(smem + wp.off_e);
+    float *sec = reinterpret_cast<float *>(smem + wp.off_ec);
+    float *sy = reinterpret_cast<float *>(smem + wp.off_y);
+    int *sn = reinterpret_cast<int *>(smem + wp.off_n);
+    auto kbuf = [&](int c) { return smem + wp.off_buf + (c & 1) * wp.buf; };
+    auto lbuf = [&](int c) { return reinterpret_cast<const float *>(smem + wp.off_buf + (c & 1) * wp.buf + wp.lam); };
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int li = lane & 15, kg = lane >> 4;
+    // block -> (pair, split): the two workgroups of a pair are 8 blocks apart
+    const int xcd = blockIdx.x & 7, qb = blockIdx.x >> 3;
+    const int split = qb % NS;
+    const int pr = (qb / NS) * 8 + xcd;
+    if (pr >= npairs)
+        return;
+    const int H = P.heads;
+    const int r = pr / H, h = pr - r * H;
+    const int unit = slot_idx ? slot_idx[r] : r;
+    if (unit < 0 || unit >= P.units) {
+        if (split == 0)
+            reject_row(P, nullptr, D, DL_FLAG_BAD_SLOT);
+        return;
+    }
+    const size_t pair = (size_t)unit * H + h;
+    if (tid == 0) {
+        // the fill count through tickets in its upper half (as merge_wy_kernel)
+        const int old = atomicAdd(P.fill + pair, 1 << 16);
+        const int n0 = old & 0xffff;
+        const bool go = n0 > 0 && n0 <= L && (mode != DL_MERGE_FULL || n0 == L);
+        if ((old >> 16) == NS - 1)
+            P.fill[pair] = go ? 0 : n0;
+        sn[0] = go ? n0 : 0;
+    }
+    __syncthreads();
+    const int n = sn[0];
+    if (n == 0)
+        return;
+    const int nch = (n + 15) >> 4;       // chunks of 16 entries
+    const size_t e0 = pair * L;
+
+    // chunk c's keys (and per-key Lam) into its buffer, entries past n left
+    // out (a direct-to-LDS load writes lane l at its wave-uniform address +
+    // size * l, so each wave takes 64 consecutive elements of a pass)
+    auto stage_chunk = [&](int c) {
+        const int cnt = (n - 16 * c) < 16 ? (n - 16 * c) : 16;
+        const int nk = cnt * D * (int)sizeof(T) / 16;
+        const uint4 *ks = reinterpret_cast<const uint4 *>(static_cast<const T *>(P.log_k) + (e0 + 16 * c) * D);
+        unsigned char *kd = kbuf(c);
+        for (int b = 64 * wave; b < nk; b += 256)
+            if (b + lane < nk)
+                load_to_lds<16>(ks + b + lane, kd + 16 * b);
+        if constexpr (PK) {
+            const int nl = cnt * D / 4;
+            const float4 *ls = reinterpret_cast<const float4 *>(P.log_g + (e0 + 16 * c) * D);
+            for (int b = 64 * wave; b < nl; b += 256)
+                if (b + lane < nl)
+                    load_to_lds<16>(ls + b + lane, kd + wp.lam + 16 * b);
+        }
+    };
+
+    // ---- loads: per-entry scalars (wave 0), R, the last entry's Lam, chunk
+    //      0's key side, then the base rows and chunk 0's values
+    float b_j = 1.f, lam_j = 0.f;
+    if (wave == 0 && lane < n) {
+        if constexpr (DELTA)
+            b_j = P.log_beta[e0 + lane];
+        if constexpr (!PK)
+            lam_j = P.log_g[e0 + lane];
+    }
+    if constexpr (DELTA) {
+        const int nt = n * (n - 1) / 2;
+        const float *ts = P.log_t + pair * packed_t_len(V, L);
+        for (int b = 64 * wave; b < nt; b += 256)
+            if (b + lane < nt)
+                load_to_lds<4>(ts + b + lane, smem + wp.off_t + 4 * b);
+    }
+    if constexpr (PK) {
+        if (wave == 0 && lane < D / 4)
+            load_to_lds<16>(reinterpret_cast<const float4 *>(P.log_g + (e0 + n - 1) * D) + lane,
+                            smem + wp.off_ll);
+    }
+    stage_chunk(0);
+    __builtin_amdgcn_sched_barrier(0);
+    float *Sp = P.base + pair * D * D;
+    const int row = split * ROWS + 16 * wave + li;
+    floatx4 st[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const float4 x = load_state4<NTS>(Sp + (size_t)row * D + 4 * kg + 16 * m);
+        st[m] = floatx4{x.x, x.y, x.z, x.w};
+    }
+    // values of chunk c on this lane: V[entry 16 c + 4 kg + rr][row], loaded
+    // as they are (the last entry again past n) and masked where used, so
+    // that nothing waits for them before then
+    const T *Vl = static_cast<const T *>(P.log_v) + e0 * D;
+    auto load_values = [&](int c, float (&vr)[4]) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int j = 16 * c + 4 * kg + rr;
+            vr[rr] = Elem<T>::load1(Vl + (size_t)(j < n ? j : n - 1) * D + row);
+        }
+    };
+    auto masked = [&](int c, const float (&vr)[4]) {
+        floatx4 v;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+            v[rr] = 16 * c + 4 * kg + rr < n ? vr[rr] : 0.f;
+        return v;
+    };
+    float vv[4];
+    load_values(0, vv);
+    __builtin_amdgcn_sched_barrier(0);
+    barrier_after_staging<NM + 4>();     // R, the last Lam row and chunk 0 staged
+
+    // ---- per-entry factors and E_c
+    if (wave == 0) {
+        if constexpr (!PK) {
+            const float lam_c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lam_j), n - 1));
+            if (lane < n) {
+                sf[lane] = b_j * fast_exp(lam_c - lam_j);
+                se[lane] = fast_exp(lam_j);
+            }
+            const float ec = fast_exp(lam_c);
+            for (int c = lane; c < D; c += 64)
+                sec[c] = ec;
+        } else {
+            if (lane < n)
+                sf[lane] = b_j;
+            for (int c = lane; c < D; c += 64)
+                sec[c] = fast_exp(sll[c]);
+        }
+    }
+    __syncthreads();
+
+    // Q[i][ch] = f_i k_i[ch] (per-key: times D(i, c) on the channel) from
+    // chunk c's buffer; 0 past n
+    auto qval = [&](int c, int i, int ch) {
+        const int ic = i < n ? i : n - 1;
+        const int il = ic - 16 * c;
+        float q = Elem<T>::load1(reinterpret_cast<const T *>(kbuf(c)) + il * D + ch) * sf[ic];
+        if constexpr (PK)
+            q *= fast_exp(sll[ch] - lbuf(c)[il * D + ch]);
+        return i < n ? q : 0.f;
+    };
+
+    floatx4 z[MAXC], yacc[MAXC][NM / NW];
+#pragma unroll
+    for (int t = 0; t < MAXC; ++t)
+#pragma unroll
+        for (int mb = 0; mb < NM / NW; ++mb)
+            yacc[t][mb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    // ---- phase A for chunk c: z_c = V_c^T - S0 Kt_c^T
+    auto phase_a = [&](int c) {
+        z[c] = masked(c, vv);
+        if constexpr (DELTA) {
+            const int j = 16 * c + li;            // this lane's entry of the A operand
+            const bool live = j < n;
+            const int jl = (live ? j : n - 1) - 16 * c;
+            const float ej = PK ? 1.f : (live ? se[16 * c + jl] : 0.f);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                if (m % 2 == 0)
+                    __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
+                const int col = 4 * kg + 16 * m;
+                float4 kt = lds_load4<T>(kbuf(c), jl * D + col);
+                if constexpr (PK) {
+                    const float4 l4 = *reinterpret_cast<const float4 *>(lbuf(c) + jl * D + col);
+                    kt.x *= fast_exp(l4.x), kt.y *= fast_exp(l4.y);
+                    kt.z *= fast_exp(l4.z), kt.w *= fast_exp(l4.w);
+                }
+                const float f = live ? -ej : 0.f;   // -Kt (head-wise: E_j; per-key: folded above)
+                z[c] = mfma16x16x4(f * kt.x, st[m][0], z[c]);
+                z[c] = mfma16x16x4(f * kt.y, st[m][1], z[c]);
+                z[c] = mfma16x16x4(f * kt.z, st[m][2], z[c]);
+                z[c] = mfma16x16x4(f * kt.w, st[m][3], z[c]);
+            }
+        }
+    };
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+        if (c >= nch)
+            break;
+        // The next chunk's key side and values load while this one is used;
+        // its buffer held chunk c - 1, consumed before the last barrier.  For
+        // chunk 0 they are issued after phase A, which waits for the base
+        // rows: issued before it, they would be waited for with them.
+        float vn[4] = {0.f, 0.f, 0.f, 0.f};
+        const bool next = c + 1 < nch;
+        if (c > 0 && next) {
+            stage_chunk(c + 1);
+            load_values(c + 1, vn);
+        }
+        phase_a(c);
+        if (c == 0 && next) {
+            stage_chunk(1);
+            load_values(1, vn);
+        }
+        // ---- Y_t += R[t rows, chunk c columns] Q_c for t <= c, on this
+        //      wave's column blocks: Y_t[16 t + 4 kg + rr][16 m + li]
+#pragma unroll
+        for (int mb = 0; mb < NM / NW; ++mb) {
+            const int m = wave * (NM / NW) + mb;
+            const int ch = 16 * m + li;
+            if constexpr (DELTA) {
+                // this lane's Q operands of the chunk's four k-steps, shared
+                // by every row block t
+                float qv[4];
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+                    qv[s4] = qval(c, 16 * c + 4 * s4 + kg, ch);
+#pragma unroll
+                for (int t = 0; t <= c; ++t) {
+                    const int j = 16 * t + li;             // this lane's row of R
+#pragma unroll
+                    for (int s4 = 0; s4 < 4; ++s4) {
+                        const int i0 = 16 * c + 4 * s4;
+                        if (i0 >= n)
+                            break;
+                        const int i = i0 + kg;
+                        // R[j][i]: 1 on the diagonal, column i's packed entry above it
+                        float rji = (i == j) ? 1.f : 0.f;
+                        if (j < i && i < n)
+                            rji = sT[i * (i - 1) / 2 + j];
+                        rji = (j < n) ? rji : 0.f;
+                        yacc[t][mb] = mfma16x16x4(rji, qv[s4], yacc[t][mb]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    yacc[c][mb][rr] = qval(c, 16 * c + 4 * kg + rr, ch);
+            }
+        }
+        if (next)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                vv[rr] = vn[rr];
+        wait_vm_all();      // the next chunk has landed in its buffer
+        __syncthreads();    // and this chunk's buffer is consumed
+    }
+
+    // ---- S0 diag(E_c), then S0 += z_t Y_t chunk by chunk
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        const float4 el = *reinterpret_cast<const float4 *>(sec + 4 * kg + 16 * m);
+        st[m][0] *= el.x;
+        st[m][1] *= el.y;
+        st[m][2] *= el.z;
+        st[m][3] *= el.w;
+    }
+#pragma unroll
+    for (int t = 0; t < MAXC; ++t) {
+        if (t >= nch)
+            break;
+        if (t > 0)
+            __syncthreads();    // the previous Y_t is consumed
+#pragma unroll
+        for (int mb = 0; mb < NM / NW; ++mb) {
+            const int ch = 16 * (wave * (NM / NW) + mb) + li;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                sy[(4 * kg + rr) * KS + ch] = yacc[t][mb][rr];
+        }
+        __syncthreads();
+        // S'^T += Y_t^T z_t^T (MFMA, accumulating in place)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            if (m % 2 == 0)
+                __builtin_amdgcn_sched_barrier(0);   // bound the LDS reads in flight
+            float a[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                a[rr] = sy[(4 * kg + rr) * KS + 16 * m + li];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                st[m] = mfma16x16x4(a[rr], z[t][rr], st[m]);
+        }
+    }
+
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+        store_state4<NTS>(Sp + (size_t)row * D + 4 * kg + 16 * m,
+                          make_float4(st[m][0], st[m][1], st[m][2], st[m][3]));
+}
+
 // ---------------------------------------------------------------------------
 #define DL_DISPATCH_M(P, FN, ...)                                                        \
     do {                                                                                 \
@@ -498,11 +846,11 @@ static void wy_launch(const Params &P, int pairs, const int *slot_idx, int mode,
 
 // d = 128: with per-key decays, one workgroup per pair, holding the pair's
 // whole base, while the chunks' z tiles fit beside it in registers (logs of
-// up to 32 entries); with head-wise decay, and for longer logs, a pair's rows
-// split over two workgroups of half the registers (twice the workgroups per
-// CU, each staging the pair's key side again: about 4% faster for GDN at 16
-// and 32 entries, 20% slower for per-key decays at 32, whose key side is
-// twice as large).  Splitting further (four workgroups of two waves) measured
+// up to 32 entries); with head-wise decay, a pair's rows split over two
+// workgroups of half the registers (twice the workgroups per CU, each
+// staging the pair's key side again: about 4% faster for GDN at 16 and 32
+// entries, 20% slower for per-key decays at 32, whose key side is twice as
+// large).  Longer logs take the chunked kernel (two workgroups per pair).  Splitting further (four workgroups of two waves) measured
 // slower everywhere: a workgroup's time is set by its chain of loads,
 // barriers and contractions, not by its share of the base.
 template <int V, int D, typename T>
@@ -521,7 +869,14 @@ static hipError_t wy_t(const Params &P, int rows, const int *slot_idx, int mode,
             else
                 wy_launch<V, D, T, 4, 2, 2>(P, pairs, slot_idx, mode, ln);
         } else {
-            wy_launch<V, D, T, 4, 1, 4>(P, pairs, slot_idx, mode, ln);
+            const WyChunkPlan wp = wy_chunk_plan(V, D, (int)sizeof(T), P.L);
+            const dim3 grid(((pairs + 7) / 8) * 8 * 2), block(256);
+            if (P.stream)
+                hipExtLaunchKernelGGL((merge_wy_chunked_kernel<V, D, T, true>), grid, block, wp.bytes,
+                                      ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode, pairs);
+            else
+                hipExtLaunchKernelGGL((merge_wy_chunked_kernel<V, D, T, false>), grid, block, wp.bytes,
+                                      ln.stream, ln.start, ln.stop, 0, P, slot_idx, mode, pairs);
         }
     } else {
         wy_launch<V, D, T, 4, 1, 4>(P, pairs, slot_idx, mode, ln);

@@ -304,8 +304,12 @@ def test_zero_rows_and_argument_errors():
 @pytest.mark.parametrize("wl,L", [(W.GDN_HYBRID.scaled(batch=3, heads=4, steps=16), 16),
                                   (W.KDA_SWEEP.scaled(batch=3, heads=4, steps=64), 64),
                                   (W.RWKV6_ADD.scaled(batch=3, heads=4, steps=32), 32),
-                                  (W.KDA_SWEEP.scaled(batch=2, heads=2, steps=13), 13)],
-                         ids=["gdn16", "kda64", "rwkv32", "kda13-partial"])
+                                  (W.KDA_SWEEP.scaled(batch=2, heads=2, steps=13), 13),
+                                  (W.GDN_HYBRID.scaled(batch=3, heads=4, steps=37), 48),
+                                  (W.KDA_SWEEP.scaled(batch=2, heads=3, steps=41), 64),
+                                  (W.KDA_SWEEP.scaled(batch=2, heads=3, steps=16), 64)],
+                         ids=["gdn16", "kda64", "rwkv32", "kda13-partial", "gdn48-partial",
+                              "kda64-partial", "kda64-one-chunk"])
 def test_wy_merge_equals_replay_merge(wl, L):
     """The MFMA WY merge and the step-by-step replay merge agree closely."""
     H, d = wl.heads, wl.d_k

@@ -277,21 +277,22 @@ merge_wy_kernel(Params P, const int *__restrict__ slot_idx, int mode, int npairs
             st[it][m] = floatx4{x.x, x.y, x.z, x.w};
         }
     }
-    // values of chunk c on this lane: V[entry 16 c + 4 kg + rr][row] (0 past n)
+    // values of chunk c on this lane: V[entry 16 c + 4 kg + rr][row], loaded
+    // as they are (the last entry again past n) and masked where used, so
+    // that nothing waits for them before then
     const T *Vl = static_cast<const T *>(P.log_v) + e0 * D;
-    auto load_values = [&](int c, floatx4 (&vv)[NIT]) {
+    auto load_values = [&](int c, float (&vr)[NIT][4]) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int row = row0 + 16 * (wave * NIT + it) + li;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int j = 16 * c + 4 * kg + rr;
-                const float x = Elem<T>::load1(Vl + (size_t)(j < n ? j : n - 1) * D + row);
-                vv[it][rr] = j < n ? x : 0.f;
+                vr[it][rr] = Elem<T>::load1(Vl + (size_t)(j < n ? j : n - 1) * D + row);
             }
         }
     };
-    floatx4 vv[NIT];
+    float vv[NIT][4];
     load_values(0, vv);
     __builtin_amdgcn_sched_barrier(0);
     // the staging has landed once at most the base and value loads are outstanding
@@ -324,12 +325,16 @@ merge_wy_kernel(Params P, const int *__restrict__ slot_idx, int mode, int npairs
     for (int c = 0; c < NE; ++c) {
         if (c >= nch)
             break;
-        floatx4 vn[NIT];
-        if (c + 1 < nch)
-            load_values(c + 1, vn);      // the next chunk's values, in flight
+        // the next chunk's values, in flight (not under a condition: past
+        // the last chunk they read the last entry again and go unused; a load
+        // under one is waited for before its register is merged)
+        float vn[NIT][4];
+        load_values(c + 1, vn);
 #pragma unroll
         for (int it = 0; it < NIT; ++it)
-            z[c][it] = vv[it];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                z[c][it][rr] = 16 * c + 4 * kg + rr < n ? vv[it][rr] : 0.f;
         if constexpr (DELTA) {
             const int j = 16 * c + li;            // this lane's entry of the A operand
             const bool live = j < n;
@@ -358,10 +363,11 @@ merge_wy_kernel(Params P, const int *__restrict__ slot_idx, int mode, int npairs
                 }
             }
         }
-        if (c + 1 < nch)
 #pragma unroll
-            for (int it = 0; it < NIT; ++it)
-                vv[it] = vn[it];
+        for (int it = 0; it < NIT; ++it)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                vv[it][rr] = vn[it][rr];
     }
 
     // ---- phase B: S0 diag(E_c), then S0 += z_c Y_c chunk by chunk
@@ -694,14 +700,18 @@ merge_wy_chunked_kernel(Params P, const int *__restrict__ slot_idx, int mode, in
         // its buffer held chunk c - 1, consumed before the last barrier.  For
         // chunk 0 they are issued after phase A, which waits for the base
         // rows: issued before it, they would be waited for with them.
-        float vn[4] = {0.f, 0.f, 0.f, 0.f};
-        const bool next = c + 1 < nch;
-        if (c > 0 && next) {
+        // The value loads are not under a condition (past the last chunk they
+        // read the last entry again and go unused): a load under one leaves
+        // its register to be merged with the other path's, and the compiler
+        // waits for every load in flight before that copy.  A chunk past the
+        // log stages nothing.
+        float vn[4];
+        if (c > 0) {
             stage_chunk(c + 1);
             load_values(c + 1, vn);
         }
         phase_a(c);
-        if (c == 0 && next) {
+        if (c == 0) {
             stage_chunk(1);
             load_values(1, vn);
         }
@@ -741,10 +751,9 @@ merge_wy_chunked_kernel(Params P, const int *__restrict__ slot_idx, int mode, in
                     yacc[c][mb][rr] = qval(c, 16 * c + 4 * kg + rr, ch);
             }
         }
-        if (next)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                vv[rr] = vn[rr];
+        for (int rr = 0; rr < 4; ++rr)
+            vv[rr] = vn[rr];
         wait_vm_all();      // the next chunk has landed in its buffer
         __syncthreads();    // and this chunk's buffer is consumed
     }

@@ -168,6 +168,7 @@ KERNEL_SOURCES = {
     "af_step_kernel": ("dl_step_af.hip",),
     "af_merge_kernel": ("dl_step_af.hip",),
     "merge_wy_kernel": ("dl_merge.hip",),
+    "merge_wy_chunked_kernel": ("dl_merge.hip",),
     "stream_probe": ("dl_probe.hip",),
 }
 SHARED_SOURCES = ("dl_common.hpp", "dl_abi.hip")
@@ -783,7 +784,9 @@ def main(argv=None):
     if others:
         out["other_paths"] = others
     merges = {}
-    for sep, mk in (("log", "merge_wy_kernel"), ("af", "af_merge_kernel")):
+    # the WY merge of logs longer than 32 entries at d = 128 is the chunked kernel
+    wy_merge = "merge_wy_chunked_kernel" if (d == 128 and L > 32) else "merge_wy_kernel"
+    for sep, mk in (("log", wy_merge), ("af", "af_merge_kernel")):
         if sep in results and results[sep]["merge_launches"]:
             u = results[sep]
             ms = u["merge_ms_total"] / 1e3

@@ -25,6 +25,33 @@
 
 namespace dl {
 
+// Eight input elements (bf16 pairs or floats) loaded as they are; converted
+// where they are used, so that the conversion does not make the compiler
+// wait for the load (and for every load issued before it) any earlier.
+template <typename T>
+__device__ __forceinline__ void load_bits8(const T *p, uint4 (&r)[2]) {
+    r[0] = reinterpret_cast<const uint4 *>(p)[0];
+    if constexpr (sizeof(T) == 4)
+        r[1] = reinterpret_cast<const uint4 *>(p)[1];
+}
+
+template <typename T>
+__device__ __forceinline__ void bits8_to_float(const uint4 (&r)[2], float *x) {
+    if constexpr (sizeof(T) == 4) {
+        x[0] = __uint_as_float(r[0].x), x[1] = __uint_as_float(r[0].y);
+        x[2] = __uint_as_float(r[0].z), x[3] = __uint_as_float(r[0].w);
+        x[4] = __uint_as_float(r[1].x), x[5] = __uint_as_float(r[1].y);
+        x[6] = __uint_as_float(r[1].z), x[7] = __uint_as_float(r[1].w);
+    } else {
+        x[0] = bf16_lo(r[0].x), x[1] = bf16_hi(r[0].x), x[2] = bf16_lo(r[0].y), x[3] = bf16_hi(r[0].y);
+        x[4] = bf16_lo(r[0].z), x[5] = bf16_hi(r[0].z), x[6] = bf16_lo(r[0].w), x[7] = bf16_hi(r[0].w);
+    }
+}
+
+}  // namespace dl
+
+namespace dl {
+
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(256) zero_kernel(uint4 *p, size_t n16) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -505,10 +532,13 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
             st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
     const int cg = lane % G, ro = lane / G, ch0 = 8 * cg;
-    float qv[8], kn[8];
-    load8<T>(q + io + ch0, qv);
+    // q and k on this lane's channels, kept as loaded until they are used: a
+    // conversion here would make the compiler wait for them, and so for the
+    // base loads issued before them, ahead of the loads below
+    uint4 qbits[2] = {}, kbits[2] = {};
+    load_bits8<T>(q + io + ch0, qbits);
     if constexpr (APPEND)
-        load8<T>(k + io + ch0, kn);
+        load_bits8<T>(k + io + ch0, kbits);
     __builtin_amdgcn_sched_barrier(0);
     if (APPEND ? (n >= L || n < 0) : (n > L || n < 0)) {
         reject_row(P, orow, D, DL_FLAG_LOG_FULL);
@@ -517,37 +547,85 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
 
     // ---- loads that need n: logged values of this wave's rows (clamped,
     //      branch-free; an empty log reads a dummy in-range address instead),
-    //      the staging, and (wave 0) the per-entry scalars and the append
+    //      the per-entry scalars and the append's inputs, then the staging.
+    //      At d = 128 every wave loads the scalars and inputs, without a
+    //      condition, ahead of the staging, so that they are in flight with the
+    //      base and nothing waits for them before wave 0 uses them (entry 0 of
+    //      an empty log is a valid address); at d = 64, where a workgroup's
+    //      loads are few, the extra loads cost more than they hide, and wave 0
+    //      loads them after the staging.
+    constexpr bool EARLY = D == 128;
     float vc[SH::ITER];       // the new entry's value on this lane's rows
 #pragma unroll
     for (int it = 0; it < SH::ITER; ++it)
         vc[it] = APPEND ? Elem<T>::load1(v + io + wave * SH::RPW + it * 8 + grp) : 0.f;
-    if (n > 0)
-        stage_log<V, D, T>(P, pair, n, smem, sp, lane, wave);
-    if (wave == 0) {
-        const int jl = lane < n ? lane : (n > 0 ? n - 1 : 0);
-        float lam_j = 0.f, b_j = 1.f;     // entry `lane`: Lam (GDN) and beta
-        float lc[8];                      // Lam_c on this lane's channels (per-key decays)
-        float g_s = 0.f, b_in = 1.f, gn[8], vv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            lc[i] = 0.f;
-        if (n > 0) {
-            if constexpr (V == GDN)
-                lam_j = P.log_g[e0 + jl];
-            if constexpr (DELTA)
-                b_j = P.log_beta[e0 + jl];
-            if constexpr (V != GDN)
-                load8<float>(P.log_g + (e0 + n - 1) * D + ch0, lc);
-        }
+    // A state without a log (an eager state's readout runs here with L = 0)
+    // has no log arrays: its early loads read this workgroup's output row
+    // instead, a valid address, and go unused (n = 0).
+    const bool has_log = L > 0;
+    const int jl = lane < n ? lane : (n > 0 ? n - 1 : 0);
+    float lam_raw = 0.f, b_raw = 1.f, g_s = 0.f, b_in = 1.f;
+    uint4 lbits[2] = {}, vbits[2] = {}, gbits[2] = {};   // Lam_{n-1}, v and g on this lane's channels
+    if constexpr (EARLY) {
+        if constexpr (V == GDN)
+            lam_raw = (has_log ? P.log_g + e0 + jl : orow)[0];
+        if constexpr (DELTA)
+            b_raw = (has_log ? P.log_beta + e0 + jl : orow)[0];
+        if constexpr (V != GDN)
+            load_bits8<float>(has_log ? P.log_g + (e0 + (n > 0 ? n - 1 : 0)) * D + ch0 : orow + ch0, lbits);
         if constexpr (APPEND) {
-            load8<T>(v + io + ch0, vv);
+            load_bits8<T>(v + io + ch0, vbits);
             if constexpr (V == GDN)
                 g_s = g[pr];
             else
-                load8<float>(g + io + ch0, gn);
+                load_bits8<float>(g + io + ch0, gbits);
             if constexpr (DELTA)
                 b_in = beta[pr];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (n > 0)
+        stage_log<V, D, T>(P, pair, n, smem, sp, lane, wave);
+    if (wave == 0) {
+        float qv[8], kn[8];
+        bits8_to_float<T>(qbits, qv);
+        if constexpr (APPEND)
+            bits8_to_float<T>(kbits, kn);
+        float lam_j = 0.f, b_j = 1.f;     // entry `lane`: Lam (GDN) and beta
+        float lc[8];                      // Lam_c on this lane's channels (per-key decays)
+        float gn[8], vv[8];
+        if constexpr (EARLY) {
+            lam_j = n > 0 ? lam_raw : 0.f;
+            b_j = n > 0 ? b_raw : 1.f;
+            bits8_to_float<float>(lbits, lc);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                lc[i] = n > 0 ? lc[i] : 0.f;
+            if constexpr (APPEND) {
+                bits8_to_float<T>(vbits, vv);
+                bits8_to_float<float>(gbits, gn);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                lc[i] = 0.f;
+            if (n > 0) {
+                if constexpr (V == GDN)
+                    lam_j = P.log_g[e0 + jl];
+                if constexpr (DELTA)
+                    b_j = P.log_beta[e0 + jl];
+                if constexpr (V != GDN)
+                    load8<float>(P.log_g + (e0 + n - 1) * D + ch0, lc);
+            }
+            if constexpr (APPEND) {
+                load8<T>(v + io + ch0, vv);
+                if constexpr (V == GDN)
+                    g_s = g[pr];
+                else
+                    load8<float>(g + io + ch0, gn);
+                if constexpr (DELTA)
+                    b_in = beta[pr];
+            }
         }
         // Lam_c, then the append of entry n: bit copies of k and v, the decay
         // accumulated through it, beta
@@ -595,6 +673,10 @@ log_step_kernel(Params P, const int *__restrict__ slot_idx, const T *__restrict_
 
     const int ct = APPEND ? n + 1 : n;   // entries the readout sees
     const int npass = (ct + PASS - 1) / PASS;
+    float qv[8], kn[8];
+    bits8_to_float<T>(qbits, qv);
+    if constexpr (APPEND)
+        bits8_to_float<T>(kbits, kn);
 
     float lam_c = 0.f, lc[8];
     if constexpr (V == GDN) {

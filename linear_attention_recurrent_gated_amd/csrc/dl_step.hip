@@ -961,10 +961,12 @@ log_step_chunked_kernel(Params P, const int *__restrict__ slot_idx, const T *__r
             st[it][m] = load_state4<NT>(Sp + (size_t)row * D + col_of(s, m, 0));
     }
     const int cg = lane % G, ro = lane / G, ch0 = 8 * cg;
-    float qv[8], kn[8];
-    load8<T>(q + io + ch0, qv);
+    // q and k on this lane's channels, kept as loaded until they are used
+    // (as in the log step kernel)
+    uint4 qbits[2] = {}, kbits[2] = {};
+    load_bits8<T>(q + io + ch0, qbits);
     if constexpr (APPEND)
-        load8<T>(k + io + ch0, kn);
+        load_bits8<T>(k + io + ch0, kbits);
     __builtin_amdgcn_sched_barrier(0);
     if (APPEND ? (n >= L || n < 0) : (n > L || n < 0)) {
         reject_row(P, orow, D, DL_FLAG_LOG_FULL);
@@ -973,12 +975,26 @@ log_step_chunked_kernel(Params P, const int *__restrict__ slot_idx, const T *__r
     const int ct = APPEND ? n + 1 : n;       // entries the readout sees
     const int na = n < CH ? n : CH;          // logged entries in the first chunk
 
-    // ---- loads that need n: this lane's rows of the new value, the first
-    //      chunk and R, and (wave 0) the per-entry scalars and the append
+    // ---- loads that need n: this lane's rows of the new value, the
+    //      per-entry scalars and the append's inputs (every wave, without a
+    //      condition, so that they fly with the base; this kernel serves logs
+    //      of more than 32 entries, so the log arrays exist), then the first
+    //      chunk and R
     float vc[SH::ITER];
 #pragma unroll
     for (int it = 0; it < SH::ITER; ++it)
         vc[it] = APPEND ? Elem<T>::load1(v + io + wave * SH::RPW + it * 8 + grp) : 0.f;
+    const int jl = lane < n ? lane : (n > 0 ? n - 1 : 0);
+    const float b_raw = P.log_beta[e0 + jl];
+    uint4 lbits[2] = {}, vbits[2] = {}, gbits[2] = {};   // Lam_{n-1}, v and g on this lane's channels
+    load_bits8<float>(P.log_g + (e0 + (n > 0 ? n - 1 : 0)) * D + ch0, lbits);
+    float b_in = 1.f;
+    if constexpr (APPEND) {
+        load_bits8<T>(v + io + ch0, vbits);
+        load_bits8<float>(g + io + ch0, gbits);
+        b_in = beta[pr];
+    }
+    __builtin_amdgcn_sched_barrier(0);
     stage_rows(P.log_k, e0, 0, na, KROW, smem + cp.off_kc, lane, wave);
     stage_rows(P.log_g, e0, 0, na, LROW, smem + cp.off_lc, lane, wave);
     {
@@ -989,19 +1005,18 @@ log_step_chunked_kernel(Params P, const int *__restrict__ slot_idx, const T *__r
                 load_to_lds<4>(ts + b + lane, smem + cp.off_t + 4 * b);
     }
     if (wave == 0) {
-        const int jl = lane < n ? lane : (n > 0 ? n - 1 : 0);
-        float b_j = 1.f, lc[8], b_in = 1.f, gn[8], vv[8];
+        float qv[8], kn[8];
+        bits8_to_float<T>(qbits, qv);
+        if constexpr (APPEND)
+            bits8_to_float<T>(kbits, kn);
+        float b_j = n > 0 ? b_raw : 1.f, lc[8], gn[8], vv[8];
+        bits8_to_float<float>(lbits, lc);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            lc[i] = 0.f;
-        if (n > 0) {
-            b_j = P.log_beta[e0 + jl];
-            load8<float>(P.log_g + (e0 + n - 1) * D + ch0, lc);
-        }
+            lc[i] = n > 0 ? lc[i] : 0.f;
         if constexpr (APPEND) {
-            load8<T>(v + io + ch0, vv);
-            load8<float>(g + io + ch0, gn);
-            b_in = beta[pr];
+            bits8_to_float<T>(vbits, vv);
+            bits8_to_float<float>(gbits, gn);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 lc[i] += gn[i];
@@ -1025,6 +1040,10 @@ log_step_chunked_kernel(Params P, const int *__restrict__ slot_idx, const T *__r
     }
     wait_vm_all();
     __syncthreads();    // 1: the first chunk, R, the new entry, per-entry factors
+    float qv[8], kn[8];
+    bits8_to_float<T>(qbits, qv);
+    if constexpr (APPEND)
+        bits8_to_float<T>(kbits, kn);
 
     // key and decay rows of entry j: the appended entry's own copies, or
     // row j - c0 of the staged chunk

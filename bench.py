@@ -264,12 +264,13 @@ def row_order(policy: str, fills: np.ndarray, L: int, wy: bool):
     log the step fills merge in place and run longer: "first" puts them
     ahead of the rest, "spread" spaces them evenly through the batch, "lpt"
     sorts every row by the work it has (merging rows, then the fullest logs
-    first); "auto" is "first" for the compact-WY log, whose in-step merge is
-    the longer one, and "spread" for the factor log."""
+    first); "auto" is "lpt" for the compact-WY log, whose in-step merge is the
+    longer one and whose step time grows with the log, so the launch ends on
+    its shortest rows, and "spread" for the factor log."""
     batch = len(fills)
     merging = np.nonzero(fills + 1 == L)[0]
     if policy == "auto":
-        policy = "first" if wy else "spread"
+        policy = "lpt" if wy else "spread"
     if policy == "natural" or not (0 < len(merging) < batch):
         return None
     if policy == "lpt":

@@ -190,3 +190,15 @@ def test_row_order_policies(policy):
     # nothing to order when no row (or every row) merges
     assert bench.row_order(policy, np.zeros(8, dtype=np.int64), L, wy=True) is None
     assert bench.row_order(policy, np.full(8, L - 1), L, wy=True) is None
+
+
+def test_row_order_auto():
+    """The default order: longest work first for the compact-WY log, the
+    merging rows spread through the batch for the factor log."""
+    rng = np.random.default_rng(7)
+    L = 32
+    fills = rng.integers(0, L, size=256)
+    assert np.array_equal(bench.row_order("auto", fills, L, wy=True),
+                          bench.row_order("lpt", fills, L, wy=True))
+    assert np.array_equal(bench.row_order("auto", fills, L, wy=False),
+                          bench.row_order("spread", fills, L, wy=False))

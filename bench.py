@@ -258,19 +258,19 @@ def merging_order(batch: int, merging, spread: bool):
 ORDERS = ("auto", "natural", "first", "spread", "lpt")
 
 
-def row_order(policy: str, fills: np.ndarray, L: int, wy: bool):
+def row_order(policy: str, fills: np.ndarray, L: int):
     """Dispatch order of a step's rows given each sequence's log fill before
     the step (all sequences active), or None for input order.  The rows whose
     log the step fills merge in place and run longer: "first" puts them
     ahead of the rest, "spread" spaces them evenly through the batch, "lpt"
     sorts every row by the work it has (merging rows, then the fullest logs
-    first); "auto" is "lpt" for the compact-WY log, whose in-step merge is the
-    longer one and whose step time grows with the log, so the launch ends on
-    its shortest rows, and "spread" for the factor log."""
+    first), so that a launch ends on its shortest rows; "auto" is "lpt" (both
+    log forms: a row's step time grows with its log, most of all over an INT8
+    base, where the base is a smaller share of the row's work)."""
     batch = len(fills)
     merging = np.nonzero(fills + 1 == L)[0]
     if policy == "auto":
-        policy = "lpt" if wy else "spread"
+        policy = "lpt"
     if policy == "natural" or not (0 < len(merging) < batch):
         return None
     if policy == "lpt":
@@ -544,7 +544,7 @@ def main(argv=None):
             full_next = np.nonzero(fills + np.isin(np.arange(Bt), act[tau]) == L)[0]
             order_p = None
             if wl.ragged and tau >= prefix and fused:
-                order = row_order(args.order, fills, L, wy=not path.startswith("af"))
+                order = row_order(args.order, fills, L)
                 if order is not None:
                     order_t = torch.from_numpy(order.astype(np.int32)).to(dev)
                     keep.append(order_t)

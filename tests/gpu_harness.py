@@ -129,7 +129,7 @@ def run_case(wl: W.Workload, L: int, paths=("eager", "log"), seed: int = 0,
                 o_full = torch.zeros((wl.units_total, H, d), dtype=torch.float32, device="cuda")
                 order = None
                 if bench_schedule and path.endswith("-fused") and len(act) == Bt:
-                    o_np = bench.row_order("auto", fills, L, wy=not path.startswith("af"))
+                    o_np = bench.row_order("auto", fills, L)
                     if o_np is not None:
                         order = torch.from_numpy(o_np.astype(np.int32)).cuda()
                 for l in range(layers):

@@ -176,7 +176,7 @@ def test_row_order_policies(policy):
     rng = np.random.default_rng(5)
     L = 32
     fills = rng.integers(0, L, size=256)
-    order = bench.row_order(policy, fills, L, wy=False)
+    order = bench.row_order(policy, fills, L)
     if policy == "natural":
         assert order is None
         return
@@ -188,17 +188,14 @@ def test_row_order_policies(policy):
     if policy == "lpt":
         assert np.all(np.diff(fills[order]) <= 0)
     # nothing to order when no row (or every row) merges
-    assert bench.row_order(policy, np.zeros(8, dtype=np.int64), L, wy=True) is None
-    assert bench.row_order(policy, np.full(8, L - 1), L, wy=True) is None
+    assert bench.row_order(policy, np.zeros(8, dtype=np.int64), L) is None
+    assert bench.row_order(policy, np.full(8, L - 1), L) is None
 
 
 def test_row_order_auto():
-    """The default order: longest work first for the compact-WY log, the
-    merging rows spread through the batch for the factor log."""
+    """The default order: longest work first, for both log forms."""
     rng = np.random.default_rng(7)
     L = 32
     fills = rng.integers(0, L, size=256)
-    assert np.array_equal(bench.row_order("auto", fills, L, wy=True),
-                          bench.row_order("lpt", fills, L, wy=True))
-    assert np.array_equal(bench.row_order("auto", fills, L, wy=False),
-                          bench.row_order("spread", fills, L, wy=False))
+    assert np.array_equal(bench.row_order("auto", fills, L),
+                          bench.row_order("lpt", fills, L))

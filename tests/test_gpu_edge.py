@@ -233,20 +233,28 @@ def test_permuted_slots_match_identity(form):
     assert torch.equal(a.base, b.base) and torch.equal(a.fill, b.fill)
 
 
-@pytest.mark.parametrize("path", ["eager", "wy", "wy-fused", "factors", "factors-fused"])
+@pytest.mark.parametrize("path", ["eager", "wy", "wy-fused", "factors", "factors-fused",
+                                  "factors-i8", "factors-fused-i8"])
 def test_row_order_changes_nothing(path):
     """Workgroups taken in a caller-given row order produce bit-identical
-    outputs, states and logs; an order entry out of range is flagged."""
+    outputs, states and logs (over an fp32 or an INT8 base); an order entry
+    out of range is flagged."""
     wl = W.GDN_LARGE.scaled(batch=7, layers=1, heads=3, steps=11)
     H, d, L, Bt = wl.heads, wl.d_k, 4, wl.batch
     form = B.DL_LOG_FACTORS if path.startswith("factors") else B.DL_LOG_WY
     Lp = 0 if path == "eager" else L
-    fused = path.endswith("-fused")
-    a = B.DecodeState(wl.variant, Bt, H, d, Lp, wl.dtype, log_form=form, merge_on_step=fused)
-    b = B.DecodeState(wl.variant, Bt, H, d, Lp, wl.dtype, log_form=form, merge_on_step=fused)
+    i8 = path.endswith("-i8")
+    fused = "-fused" in path
+    kw = dict(base_format=B.DL_BASE_I8, kept_channels=8) if i8 else {}
+    a = B.DecodeState(wl.variant, Bt, H, d, Lp, wl.dtype, log_form=form, merge_on_step=fused, **kw)
+    b = B.DecodeState(wl.variant, Bt, H, d, Lp, wl.dtype, log_form=form, merge_on_step=fused, **kw)
     S0 = torch.from_numpy(W.initial_state(wl)).cuda()
-    a.base.copy_(S0)
-    b.base.copy_(S0)
+    if i8:
+        a.import_base(S0)
+        b.import_base(S0)
+    else:
+        a.base.copy_(S0)
+        b.base.copy_(S0)
     rng = np.random.default_rng(3)
     for tau in range(wl.steps):
         _, args = _inputs(wl, tau)

@@ -187,9 +187,16 @@ def test_row_order_policies(policy):
         assert np.array_equal(np.sort(pos), np.arange(len(merging)))
     if policy == "lpt":
         assert np.all(np.diff(fills[order]) <= 0)
-    # nothing to order when no row (or every row) merges
+    # nothing to order when every row has the same work
     assert bench.row_order(policy, np.zeros(8, dtype=np.int64), L) is None
     assert bench.row_order(policy, np.full(8, L - 1), L) is None
+    # with no row merging, the orders built around merging rows keep the
+    # batch order and longest work first still sorts by log length
+    few = np.array([3, 0, 7, 7, 1, 5, 0, 2])
+    if policy in ("lpt", "auto"):
+        assert np.array_equal(bench.row_order(policy, few, L), [2, 3, 5, 0, 7, 4, 1, 6])
+    else:
+        assert bench.row_order(policy, few, L) is None
 
 
 def test_row_order_auto():

@@ -71,7 +71,12 @@ def _compare_codes(gpu, ref, X, label):
     bad = (diff != 0) & ~(band & (np.abs(diff) <= 1))
     assert not bad.any(), f"{label}: {int(bad.sum())} codes differ away from a rounding boundary"
     assert np.allclose(gs, rs, rtol=1e-5, atol=0), f"{label}: scales"
-    assert np.allclose(gh, rh, rtol=1e-5, atol=1e-7), f"{label}: kept values"
+    # kept values are fp32 entries of the merged state: the state's bar,
+    # per pair relative to max(1, max |S|)
+    if gh.size:
+        scale = np.maximum(1.0, np.abs(X).reshape(len(X), -1).max(axis=1))[:, None, None]
+        kdev = float((np.abs(gh.astype(np.float64) - rh) / scale).max())
+        assert kdev <= TOL, f"{label}: kept values off by {kdev:.2e}"
     return int((diff != 0).sum()), int(band.sum())
 
 
@@ -128,6 +133,9 @@ CASES = [
     (W.GATED.scaled(batch=2, heads=2, steps=19, state_std=0.02), 8, 4),
     (W.TINY_GDN.scaled(batch=2, heads=2, steps=20, state_std=0.5), 5, 0),
     (W.GDN_LARGE.scaled(batch=5, layers=1, heads=2, steps=14), 4, 8),       # ragged logs
+    # logs of 17-32 entries (their own kernel builds)
+    (W.GDN_HYBRID.scaled(batch=3, heads=4, steps=56), 24, 8),
+    (W.GDN_LARGE.scaled(batch=5, layers=1, heads=2, steps=45), 20, 8),      # ragged logs
 ]
 
 
